@@ -1,0 +1,171 @@
+// C ABI of libattn.so: argument validation and dispatch to the HIP kernels.
+// Every check happens before anything is launched, so a call that returns an
+// error status has written nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace attn {
+
+namespace {
+thread_local char g_err[512] = "";
+}
+
+attn_status set_error(attn_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+attn_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(ATTN_E_DEVICE, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+}  // namespace attn
+
+using namespace attn;
+
+extern "C" const char* attn_last_error(void) { return g_err; }
+
+extern "C" attn_status attn_prefill(attn_dtype dt, const void* q, const void* k, const void* v, int B, int Hq,
+                                    int Hkv, int64_t S, int64_t T, int D, int causal, float scale, float* o,
+                                    float* lse, void* stream) {
+  if (dt != ATTN_BF16 && dt != ATTN_F32)
+    return set_error(ATTN_E_UNSUPPORTED, "prefill: dtype must be ATTN_BF16 or ATTN_F32 (got %d)", (int)dt);
+  if (D != 64 && D != 128) return set_error(ATTN_E_UNSUPPORTED, "prefill: D must be 64 or 128 (got %d)", D);
+  if (B < 0 || S < 0 || T < 0 || Hq <= 0 || Hkv <= 0)
+    return set_error(ATTN_E_INVALID, "prefill: negative or zero sizes (B=%d Hq=%d Hkv=%d S=%lld T=%lld)", B, Hq,
+                     Hkv, (long long)S, (long long)T);
+  if (Hq % Hkv) return set_error(ATTN_E_INVALID, "prefill: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (causal != 0 && causal != 1) return set_error(ATTN_E_INVALID, "prefill: causal must be 0 or 1");
+  if (!isfinite(scale)) return set_error(ATTN_E_INVALID, "prefill: scale must be finite");
+  if (B == 0 || S == 0) return ATTN_OK;
+  if (!q || !o || (T > 0 && (!k || !v))) return set_error(ATTN_E_INVALID, "prefill: null device pointer");
+  PrefillArgs a{};
+  a.q = q;
+  a.k = T > 0 ? k : q;
+  a.v = T > 0 ? v : q;
+  a.o = o;
+  a.lse = lse;
+  a.q_ss = (int64_t)Hq * D;
+  a.q_sb = S * a.q_ss;
+  a.k_ss = (int64_t)Hkv * D;
+  a.k_sb = T * a.k_ss;
+  a.o_ss = a.q_ss;
+  a.o_sb = a.q_sb;
+  a.l_sh = S;
+  a.l_sb = (int64_t)Hq * S;
+  a.n_q = S;
+  a.n_k = T;
+  a.q_abs0 = T - S;
+  a.k_abs0 = 0;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.causal = causal;
+  a.accumulate = 0;
+  a.scale_log2 = scale * kLog2e;
+  if (B > 65535 || Hkv > 65535) return set_error(ATTN_E_UNSUPPORTED, "prefill: B and Hkv must be <= 65535");
+  return dt == ATTN_BF16 ? launch_prefill_bf16(a, D, (hipStream_t)stream)
+                         : launch_prefill_f32(a, D, (hipStream_t)stream);
+}
+
+extern "C" size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len, int num_splits) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_kv_len < 0 || num_splits < 0) return 0;
+  return decode_workspace_bytes(B, Hq, D, plan_decode(B, Hq, Hkv, max_kv_len, num_splits));
+}
+
+extern "C" attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, const void* k_cache,
+                                           const void* v_cache, const float* k_scale, const float* v_scale,
+                                           const int32_t* page_table, int max_pages, int page_size, int num_pages,
+                                           const int32_t* kv_lens, int max_kv_len, int B, int Hq, int Hkv, int D,
+                                           float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                                           float* o, float* lse, void* stream) {
+  if (kv_dt != ATTN_BF16 && kv_dt != ATTN_INT8 && kv_dt != ATTN_FP8_E4M3)
+    return set_error(ATTN_E_UNSUPPORTED, "decode: KV dtype must be bf16, int8 or fp8 e4m3 (got %d)", (int)kv_dt);
+  if (D != 64 && D != 128) return set_error(ATTN_E_UNSUPPORTED, "decode: D must be 64 or 128 (got %d)", D);
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || max_kv_len < 0 || num_splits < 0)
+    return set_error(ATTN_E_INVALID, "decode: invalid sizes");
+  if (Hq % Hkv) return set_error(ATTN_E_INVALID, "decode: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G > 8) return set_error(ATTN_E_UNSUPPORTED, "decode: at most 8 query heads per KV head (got %d)", G);
+  if (!isfinite(scale)) return set_error(ATTN_E_INVALID, "decode: scale must be finite");
+  if (B == 0) return ATTN_OK;
+  if (!q || !k_cache || !v_cache || !kv_lens || !o) return set_error(ATTN_E_INVALID, "decode: null device pointer");
+  if (kv_dt != ATTN_BF16 && (!k_scale || !v_scale))
+    return set_error(ATTN_E_INVALID, "decode: quantised KV needs k_scale and v_scale");
+  int shift = 0;
+  if (page_table) {
+    if (page_size < 16 || (page_size & (page_size - 1)))
+      return set_error(ATTN_E_INVALID, "decode: paged mode needs a power-of-two page_size >= 16 (got %d)",
+                       page_size);
+    if (max_pages <= 0 || num_pages <= 0) return set_error(ATTN_E_INVALID, "decode: max_pages/num_pages must be > 0");
+    if ((int64_t)max_pages * page_size < max_kv_len)
+      return set_error(ATTN_E_INVALID, "decode: max_kv_len %d exceeds max_pages*page_size", max_kv_len);
+    while ((1 << shift) < page_size) ++shift;
+  } else {
+    if (page_size < max_kv_len)
+      return set_error(ATTN_E_INVALID, "decode: contiguous cache needs page_size >= max_kv_len");
+  }
+  const DecodePlan plan = plan_decode(B, Hq, Hkv, max_kv_len, num_splits);
+  const size_t need = decode_workspace_bytes(B, Hq, D, plan);
+  if (!workspace || workspace_bytes < need)
+    return set_error(ATTN_E_INVALID, "decode: workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  if (((uintptr_t)workspace) & 255) return set_error(ATTN_E_INVALID, "decode: workspace must be 256-byte aligned");
+  if (plan.n_splits > 65535 || Hkv > 65535 || B > 65535)
+    return set_error(ATTN_E_UNSUPPORTED, "decode: grid too large");
+  DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.page_table = page_table;
+  a.max_pages = max_pages;
+  a.page_size = page_size;
+  a.page_shift = shift;
+  a.kv_lens = kv_lens;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.chunk = plan.chunk;
+  a.sub_chunk = plan.sub_chunk;
+  a.n_splits = plan.n_splits;
+  a.scale_log2 = scale * kLog2e;
+  const size_t rows = (size_t)plan.n_splits * (size_t)B * (size_t)Hq;
+  a.part_o = (float*)workspace;
+  a.part_lse = (float*)((char*)workspace + (rows * (size_t)D * sizeof(float) + 255) / 256 * 256);
+  hipStream_t s = (hipStream_t)stream;
+  attn_status st = launch_decode_split(kv_dt, a, D, G, s);
+  if (st != ATTN_OK) return st;
+  return launch_merge(plan.n_splits, a.part_o, a.part_lse, (int64_t)B * Hq, D, o, lse, s);
+}
+
+extern "C" attn_status attn_merge_partials(int n, const float* o_parts, const float* lse_parts, int64_t R, int D,
+                                           float* o, float* lse, void* stream) {
+  if (n < 0 || R < 0) return set_error(ATTN_E_INVALID, "merge: negative sizes");
+  if (D < 1 || D > 1024) return set_error(ATTN_E_UNSUPPORTED, "merge: D must be in 1..1024 (got %d)", D);
+  if (R == 0) return ATTN_OK;
+  if (!o || (n > 0 && (!o_parts || !lse_parts))) return set_error(ATTN_E_INVALID, "merge: null device pointer");
+  return launch_merge(n, o_parts, lse_parts, R, D, o, lse, (hipStream_t)stream);
+}

@@ -1,0 +1,93 @@
+// Internal declarations of libattn.so (not installed; the public ABI is include/attn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "attn.h"
+
+namespace attn {
+
+// ---------------------------------------------------------------- vector types
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- errors
+attn_status set_error(attn_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+attn_status check_launch(const char* what);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+// ---------------------------------------------------------------- prefill
+// One launch computes a block of n_q queries against a block of n_k keys for
+// every (sequence, KV head).  Local query i sits at absolute position
+// q_abs0 + i, local key j at k_abs0 + j; under `causal` key j is visible to
+// query i iff k_abs0 + j <= q_abs0 + i.  With `accumulate`, the block's
+// (O, lse) is merged by log-sum-exp into the (O, lse) already in memory.
+// Element strides: q/o [b, s, h, d] with head stride D; k/v [b, t, hk, d];
+// lse [b, h, s] with position stride 1.
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* o;
+  float* lse;  // may be null unless accumulate
+  int64_t q_sb, q_ss;
+  int64_t k_sb, k_ss;
+  int64_t o_sb, o_ss;
+  int64_t l_sb, l_sh;
+  int64_t n_q, n_k;
+  int64_t q_abs0, k_abs0;
+  int B, Hq, Hkv, G;
+  int causal;
+  int accumulate;
+  float scale_log2;  // scale * log2(e)
+};
+
+// Launchers: validate nothing (the ABI layer did), launch on `stream`.
+attn_status launch_prefill_bf16(const PrefillArgs& a, int D, hipStream_t stream);
+attn_status launch_prefill_f32(const PrefillArgs& a, int D, hipStream_t stream);
+
+// ---------------------------------------------------------------- decode
+struct DecodeArgs {
+  const void* q;  // [B, Hq, D] bf16
+  const void* k;  // cache
+  const void* v;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* page_table;  // null: contiguous
+  int max_pages;
+  int page_size;
+  int page_shift;  // log2(page_size) when paged
+  const int32_t* kv_lens;
+  int B, Hq, Hkv;
+  int chunk;     // tokens per split (multiple of 16)
+  int sub_chunk; // tokens scored into LDS at once (multiple of 16, <= chunk)
+  int n_splits;  // splits per sequence in the grid
+  float scale_log2;
+  float* part_o;    // [n_splits, B*Hq, D]
+  float* part_lse;  // [n_splits, B*Hq]
+};
+
+struct DecodePlan {
+  int chunk;
+  int sub_chunk;
+  int n_splits;
+};
+DecodePlan plan_decode(int B, int Hq, int Hkv, int max_kv_len, int num_splits);
+size_t decode_workspace_bytes(int B, int Hq, int D, const DecodePlan& p);
+
+attn_status launch_decode_split(attn_dtype kv_dt, const DecodeArgs& a, int D, int G, hipStream_t stream);
+
+// ---------------------------------------------------------------- merge
+attn_status launch_merge(int n, const float* o_parts, const float* lse_parts, int64_t R, int D, float* o,
+                         float* lse, hipStream_t stream);
+
+}  // namespace attn

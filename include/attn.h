@@ -1,0 +1,202 @@
+/*
+ * attn.h -- C ABI of libattn.so: exact scaled-dot-product attention for one
+ * AMD Instinct MI355X (gfx950), computed blockwise without materialising the
+ * S x T score matrix.
+ *
+ *   O = softmax(scale * Q K^T + mask) V,   lse = log sum_j exp(scale * q.k_j)
+ *
+ * Conventions shared by every call
+ *  - Sizes are element counts.  Tensors are dense, C-contiguous, in the
+ *    layouts given per call.  Every pointer is owned by the caller; the
+ *    library keeps none after the call returns.
+ *  - Device calls are asynchronous on `stream` (a hipStream_t; NULL = the
+ *    null stream).  A kernel fault surfaces at the caller's next
+ *    synchronisation.  Outputs must not alias inputs.
+ *  - Arguments are validated before anything is launched; on any non-OK
+ *    status nothing has been written.  attn_last_error() then returns a
+ *    message for the calling thread.
+ *  - Grouped-query attention: G = Hq / Hkv (Hq must be a multiple of Hkv) and
+ *    query head h reads KV head floor(h / G).  (Opt-GQA: LLM-CoOpt summary,
+ *    "Methodology" item 2; the head-to-group mapping itself is not on the
+ *    page: contiguous groups are the reading taken.)
+ *  - Causal masking is bottom-right aligned: with S queries and T keys,
+ *    query i sits at absolute position i + T - S and sees key j iff
+ *    j <= i + T - S (absolute position = past length + local index: ONNX
+ *    Runtime PR #33328 analysis, section 1).  A query row that sees no key
+ *    gets O = 0 and lse = -inf.
+ *  - lse is the natural-log log-sum-exp of the scaled scores of the visible
+ *    keys; it is what makes partial results mergeable (ONNX Runtime PR
+ *    #28695 analysis, section 2, reduce phase).
+ *  - Supported head dims: D = 64 or 128.  scale is explicit; callers
+ *    usually pass 1/sqrt(D).
+ *  - B == 0 or S == 0 (or R == 0) is a no-op returning ATTN_OK.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_E_INVALID = 1,     /* null required pointer, bad size, Hq % Hkv != 0, non-finite scale,
+                             non-pinned host memory, workspace too small */
+  ATTN_E_UNSUPPORTED = 2, /* head dim or dtype not supported by this call */
+  ATTN_E_BUDGET = 3,      /* attn_stream_*: the smallest sub-task does not fit the budget */
+  ATTN_E_DEVICE = 4       /* HIP launch, allocation or copy error */
+} attn_status;
+
+typedef enum attn_dtype {
+  ATTN_F32 = 0,       /* IEEE binary32 */
+  ATTN_BF16 = 1,      /* bfloat16 (upper half of binary32) */
+  ATTN_FP8_E4M3 = 2,  /* OCP 8-bit E4M3 "fn": bias 7, no infinities, 0x7F/0xFF are NaN */
+  ATTN_INT8 = 3       /* signed 8-bit code, value = code * scale */
+} attn_dtype;
+
+/*
+ * Tiled prefill: exact attention of S queries against T keys per sequence,
+ * one pass over K/V tiles with an online softmax (running row max and sum),
+ * the P.V product accumulated in fp32.  (Tiled computation with online
+ * softmax and fused SV accumulation: ONNX Runtime PR #28695 analysis,
+ * section 1; GQA: LLM-CoOpt "Methodology" item 2.)
+ *
+ *   dt      ATTN_F32 (fp32 inputs, fp32 arithmetic) or ATTN_BF16 (bf16
+ *           inputs, bf16 matrix-core products, fp32 accumulation/softmax).
+ *   q       device, [B, S, Hq, D] of dt
+ *   k, v    device, [B, T, Hkv, D] of dt
+ *   causal  0 or 1 (bottom-right, see above)
+ *   o       device, [B, S, Hq, D] fp32 (written)
+ *   lse     device, [B, Hq, S] fp32 (written), or NULL
+ * Errors: ATTN_E_INVALID, ATTN_E_UNSUPPORTED (D, dt), ATTN_E_DEVICE.
+ * T == 0 gives O = 0, lse = -inf.
+ */
+attn_status attn_prefill(attn_dtype dt, const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                         int64_t S, int64_t T, int D, int causal, float scale, float* o, float* lse, void* stream);
+
+/*
+ * Workspace bytes attn_decode_splitkv needs for these sizes (num_splits as
+ * passed to it; 0 = automatic).  Pure host arithmetic; no device access.
+ */
+size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len, int num_splits);
+
+/*
+ * Split-KV ("flash") decoding of one query token per sequence against a KV
+ * cache: the KV sequence of each (sequence, KV head) is cut into chunks, each
+ * chunk yields a normalised partial output and its lse, and the partials are
+ * merged exactly by log-sum-exp.  (Flash decoding: ONNX Runtime PR #28695
+ * analysis, section 2; 512-token pages: LLM-CoOpt "Methodology" item 3;
+ * FP8 / INT8 caches dequantised on the fly: LLM-CoOpt "Methodology" item 1,
+ * ONNX Runtime PR #28695 analysis, introduction and section 1.)
+ *
+ *   kv_dt       ATTN_BF16, ATTN_INT8 or ATTN_FP8_E4M3 (element type of the caches)
+ *   q           device, [B, Hq, D] bf16
+ *   k_cache,
+ *   v_cache     device.  Paged (page_table != NULL): [num_pages, Hkv, page_size, D].
+ *               Contiguous (page_table == NULL): [B, Hkv, page_size, D], i.e.
+ *               one page of page_size >= max_kv_len tokens per sequence.
+ *   k_scale,
+ *   v_scale     device fp32.  int8: per token and KV head, shaped like the
+ *               cache without D ([num_pages or B, Hkv, page_size]).
+ *               fp8: per KV head, [Hkv].  bf16: NULL.
+ *   page_table  device int32 [B, max_pages]: physical page of logical page
+ *               t / page_size of sequence b; entries past the sequence's
+ *               last page are never read.  Paged mode needs page_size a power
+ *               of two and a multiple of 16.
+ *   kv_lens     device int32 [B]: tokens of each sequence (0..max_kv_len).
+ *   max_kv_len  host int: upper bound of kv_lens (sizes the split plan).
+ *   num_splits  0 = automatic (enough chunks to fill the GPU), else the
+ *               maximum number of chunks per sequence.
+ *   workspace   device, >= attn_decode_workspace_size(...) bytes, 256-byte
+ *               aligned; scratch for the partials, owned by the caller, not
+ *               read before being written.
+ *   o           device [B, Hq, D] fp32 (written); lse device [B, Hq] fp32 or NULL.
+ * A sequence with kv_lens[b] == 0 gets O = 0, lse = -inf.
+ * Errors: ATTN_E_INVALID, ATTN_E_UNSUPPORTED (D, kv_dt, G > 8), ATTN_E_DEVICE.
+ */
+attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, const void* k_cache, const void* v_cache,
+                                const float* k_scale, const float* v_scale, const int32_t* page_table,
+                                int max_pages, int page_size, int num_pages, const int32_t* kv_lens,
+                                int max_kv_len, int B, int Hq, int Hkv, int D, float scale, int num_splits,
+                                void* workspace, size_t workspace_bytes, float* o, float* lse, void* stream);
+
+/*
+ * Exact log-sum-exp merge of n partial results of the same R rows:
+ *   M = max_c lse_c;  w_c = exp(lse_c - M);
+ *   O = sum_c w_c O_c / sum_c w_c;  lse = M + log sum_c w_c.
+ * A partial with lse = -inf is empty and carries no weight; all empty gives
+ * O = 0, lse = -inf.  (Reduce phase of flash decoding: ONNX Runtime PR
+ * #28695 analysis, section 2; exact recombination of independent
+ * sub-results: Stream-CQSA summary, "Methodology" item 2.)
+ *
+ *   o_parts   device [n, R, D] fp32, each normalised by its own softmax sum
+ *   lse_parts device [n, R] fp32 (natural log)
+ *   o         device [R, D] fp32; lse device [R] fp32 or NULL.
+ * D may be any value in 1..1024.  n == 0 gives O = 0, lse = -inf.
+ */
+attn_status attn_merge_partials(int n, const float* o_parts, const float* lse_parts, int64_t R, int D, float* o,
+                                float* lse, void* stream);
+
+/* Counters of a budgeted streaming run (or of its plan). */
+typedef struct attn_stream_report {
+  int64_t tasks;             /* (query block, key block) sub-tasks */
+  int64_t h2d_bytes;         /* host -> device bytes */
+  int64_t d2h_bytes;         /* device -> host bytes */
+  int64_t peak_device_bytes; /* device bytes the library held at once */
+  int64_t block_q;           /* query positions per block */
+  int64_t block_k;           /* key positions per block */
+  double wall_s;             /* whole call, seconds (0 for a plan) */
+  double kernel_s;           /* summed sub-task kernel time, seconds (0 for a plan) */
+} attn_stream_report;
+
+/*
+ * Budgeted streaming prefill in the manner of Stream-CQSA: the (query block,
+ * key block) work of exact attention is split into independent sub-tasks
+ * sized so that every device byte the call holds stays within
+ * device_budget_bytes; Q/K/V blocks are streamed from pinned host memory on a
+ * copy stream, overlapped with compute, each sub-task's partial result is
+ * merged by log-sum-exp into the resident output block, and finished output
+ * blocks are copied back.  (Stream-CQSA summary: "Key contributions",
+ * "Methodology" items 2-4, "Results & findings": memory grows with the block
+ * size, not with the sequence length.)  Blocks are rectangular: each
+ * causally visible (query block, key block) pair is one sub-task and fully
+ * masked pairs are never scheduled.
+ *
+ *   dt            ATTN_BF16 or ATTN_F32
+ *   q_host        pinned host [B, S, Hq, D]; k_host, v_host pinned host [B, T, Hkv, D]
+ *   block_q,
+ *   block_k       0 = chosen from the budget; otherwise forced (must fit)
+ *   o_host        pinned host [B, S, Hq, D] fp32; lse_host pinned host [B, Hq, S] fp32 or NULL
+ *   report        NULL or filled on success
+ * Synchronous: returns after all results are in host memory and every
+ * device byte it allocated is freed.  Uses the current HIP device.
+ * Errors: ATTN_E_INVALID (incl. non-pinned host memory), ATTN_E_UNSUPPORTED,
+ * ATTN_E_BUDGET (nothing fits), ATTN_E_DEVICE.
+ */
+attn_status attn_stream_budgeted(attn_dtype dt, const void* q_host, const void* k_host, const void* v_host, int B,
+                                 int Hq, int Hkv, int64_t S, int64_t T, int D, int causal, float scale,
+                                 size_t device_budget_bytes, int64_t block_q, int64_t block_k, float* o_host,
+                                 float* lse_host, attn_stream_report* report);
+
+/*
+ * The plan attn_stream_budgeted would execute, computed on the host only (no
+ * device access).  tasks (nullable) receives up to cap triples
+ * (sequence b, query block index, key block index) in execution order;
+ * plan (nullable) receives the counters (wall_s = kernel_s = 0).
+ * Errors: ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_BUDGET.
+ */
+attn_status attn_stream_plan(attn_dtype dt, int B, int Hq, int Hkv, int64_t S, int64_t T, int D, int causal,
+                             size_t device_budget_bytes, int64_t block_q, int64_t block_k, int64_t* tasks,
+                             int64_t cap, attn_stream_report* plan);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

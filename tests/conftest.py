@@ -19,3 +19,7 @@ def orc():
 
     oracle.load()
     return oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)

@@ -1,0 +1,167 @@
+"""CPU-only checks of libattn.so: it loads, exports every symbol declared in
+include/attn.h, validates arguments before touching a device, and its
+host-only stream planner covers every causally visible (query, key) pair
+exactly once within the device budget."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import exact_long_context_tiled_amd as attn
+from exact_long_context_tiled_amd import AttnError
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    txt = open(os.path.join(ROOT, "include", "attn.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z_0-9]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = attn.lib()
+    syms = _declared_symbols()
+    assert set(syms) >= {"attn_prefill", "attn_decode_splitkv", "attn_merge_partials", "attn_stream_budgeted",
+                         "attn_stream_plan", "attn_decode_workspace_size", "attn_last_error"}
+    for s in syms:
+        assert hasattr(L, s), s
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_prefill_validation_before_any_launch():
+    L = attn.lib()
+    # unsupported head dim
+    assert L.attn_prefill(1, None, None, None, 1, 4, 2, 8, 8, 96, 1, 0.1, None, None, None) == 2
+    assert "D must be 64 or 128" in attn.last_error()
+    # Hq not a multiple of Hkv
+    assert L.attn_prefill(1, None, None, None, 1, 5, 2, 8, 8, 64, 1, 0.1, None, None, None) == 1
+    # unsupported dtype for prefill
+    assert L.attn_prefill(3, None, None, None, 1, 4, 2, 8, 8, 64, 1, 0.1, None, None, None) == 2
+    # non-finite scale
+    assert L.attn_prefill(1, None, None, None, 1, 4, 2, 8, 8, 64, 1, float("nan"), None, None, None) == 1
+    # null pointers with real work
+    assert L.attn_prefill(1, None, None, None, 1, 4, 2, 8, 8, 64, 1, 0.1, None, None, None) == 1
+    # empty work is a no-op even with null pointers
+    assert L.attn_prefill(1, None, None, None, 0, 4, 2, 8, 8, 64, 1, 0.1, None, None, None) == 0
+    assert L.attn_prefill(1, None, None, None, 2, 4, 2, 0, 8, 64, 1, 0.1, None, None, None) == 0
+
+
+def test_decode_and_merge_validation():
+    L = attn.lib()
+    args = dict(q=None, k=None, v=None, ks=None, vs=None, pt=None, maxp=0, ps=512, npg=0, lens=None, maxlen=100,
+                B=2, Hq=32, Hkv=8, D=128, scale=0.1, ns=0, ws=None, wsb=0, o=None, lse=None, st=None)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.attn_decode_splitkv(kw.get("dt", 1), a["q"], a["k"], a["v"], a["ks"], a["vs"], a["pt"], a["maxp"],
+                                     a["ps"], a["npg"], a["lens"], a["maxlen"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                     a["scale"], a["ns"], a["ws"], a["wsb"], a["o"], a["lse"], a["st"])
+
+    assert call(dt=0) == 2  # fp32 caches are not a decode dtype
+    assert call(D=80) == 2
+    assert call(Hq=36, Hkv=4) == 2  # G = 9 > 8
+    assert call(Hq=30) == 1
+    assert call() == 1  # null pointers
+    assert call(B=0) == 0
+    # merge
+    assert L.attn_merge_partials(2, None, None, 10, 0, None, None, None) == 2
+    assert L.attn_merge_partials(2, None, None, 10, 64, None, None, None) == 1
+    assert L.attn_merge_partials(2, None, None, 0, 64, None, None, None) == 0
+    # workspace sizing is pure host arithmetic and monotone in the length
+    a = attn.decode_workspace_size(8, 32, 8, 128, 4096)
+    b = attn.decode_workspace_size(8, 32, 8, 128, 32768)
+    assert 0 < a <= b and a % 256 == 0
+    assert attn.decode_workspace_size(8, 32, 8, 128, 32768, num_splits=4) == 2 * (
+        ((4 * 8 * 32 * 128 * 4 + 255) // 256 * 256 + (4 * 8 * 32 * 4 + 255) // 256 * 256) // 2)
+
+
+def _coverage(tasks, rep, S, T, causal, B):
+    bq, bk = rep["block_q"], rep["block_k"]
+    nqb = (S + bq - 1) // bq
+    cover = np.zeros((B, S, max(T, 1)), dtype=np.int32)
+    per_block = np.zeros((B, nqb), dtype=np.int32)
+    empty_block = np.zeros((B, nqb), dtype=np.int32)
+    for b, qb, kb in tasks:
+        per_block[b, qb] += 1
+        q0, q1 = qb * bq, min(S, (qb + 1) * bq)
+        if kb < 0:
+            empty_block[b, qb] += 1
+            continue
+        k0, k1 = kb * bk, min(T, (kb + 1) * bk)
+        i = np.arange(q0, q1)[:, None]
+        j = np.arange(k0, k1)[None, :]
+        vis = (j <= i + T - S) if causal else np.ones((q1 - q0, k1 - k0), bool)
+        assert vis.any(), "a scheduled task must contain at least one visible pair"
+        cover[b, q0:q1, k0:k1] += 1
+    i = np.arange(S)[:, None]
+    j = np.arange(max(T, 1))[None, :]
+    vis = ((j <= i + T - S) if causal else np.ones((S, max(T, 1)), bool)) & (j < T)
+    for b in range(B):
+        # every visible pair lies in exactly one task's rectangle; no rectangle overlaps another
+        assert np.all(cover[b][vis] == 1)
+        assert np.all(cover[b] <= 1)
+        # every query block is written by at least one task; a block gets an empty task
+        # exactly when none of its rows sees any key, and then it has no other task
+        assert np.all(per_block[b] >= 1)
+        for qb in range(nqb):
+            sees = vis[qb * bq:min(S, (qb + 1) * bq)].any()
+            assert empty_block[b, qb] == (0 if sees else 1)
+            if not sees:
+                assert per_block[b, qb] == 1
+
+
+@pytest.mark.parametrize("S,T,causal,bq,bk", [(300, 300, True, 64, 32), (100, 260, True, 32, 64),
+                                                (260, 100, True, 64, 32), (97, 131, False, 32, 64),
+                                                (50, 0, True, 16, 16), (1, 500, True, 128, 64)])
+def test_stream_plan_covers_visible_pairs_exactly_once(S, T, causal, bq, bk):
+    B = 2
+    tasks, rep = attn.stream_plan("bf16", B, 8, 2, S, T, 64, causal=causal, budget=1 << 40, block_q=bq,
+                                  block_k=bk)
+    assert rep["tasks"] == len(tasks)
+    _coverage(tasks, rep, S, T, causal, B)
+
+
+@pytest.mark.parametrize("budget", [2 ** 22, 2 ** 24, 2 ** 26, 2 ** 30])
+def test_stream_plan_fits_budget_and_covers(budget):
+    S = T = 3000
+    tasks, rep = attn.stream_plan("bf16", 1, 8, 2, S, T, 128, causal=True, budget=budget)
+    assert rep["peak_device_bytes"] <= budget
+    _coverage(tasks, rep, S, T, True, 1)
+
+
+def test_stream_plan_memory_tracks_block_size_not_length():
+    """Device bytes depend on the chosen blocks, not on the sequence length."""
+    reps = [attn.stream_plan("bf16", 1, 32, 8, n, n, 128, causal=True, budget=4_000_000_000, block_q=8192,
+                             block_k=4096, with_tasks=False)[1] for n in (1 << 16, 1 << 18, 1 << 20)]
+    assert len({r["peak_device_bytes"] for r in reps}) == 1
+    small = attn.stream_plan("bf16", 1, 32, 8, 1 << 20, 1 << 20, 128, budget=4_000_000_000, block_q=4096,
+                             block_k=4096, with_tasks=False)[1]
+    assert small["peak_device_bytes"] < reps[0]["peak_device_bytes"]
+
+
+def test_stream_plan_million_token_workload():
+    S = T = 1 << 20
+    budget = 4_000_000_000
+    _, rep = attn.stream_plan("bf16", 1, 32, 8, S, T, 128, causal=True, budget=budget, with_tasks=False)
+    assert rep["peak_device_bytes"] <= budget
+    assert rep["block_q"] >= 32768 and rep["block_k"] >= 4096
+    # every Q byte goes up once; O + lse come back once
+    assert rep["d2h_bytes"] == S * 32 * 128 * 4 + S * 32 * 4
+    assert rep["h2d_bytes"] >= S * 32 * 128 * 2 + 2 * T * 8 * 128 * 2
+
+
+def test_stream_budget_errors():
+    with pytest.raises(AttnError) as e:
+        attn.stream_plan("bf16", 1, 32, 8, 1 << 20, 1 << 20, 128, budget=1 << 16)
+    assert e.value.status == 3
+    with pytest.raises(AttnError) as e:
+        attn.stream_plan("bf16", 1, 32, 8, 4096, 4096, 128, budget=1 << 22, block_q=4096, block_k=4096)
+    assert e.value.status == 3
+    with pytest.raises(AttnError) as e:
+        attn.stream_plan("bf16", 1, 32, 8, 4096, 4096, 96, budget=1 << 30)
+    assert e.value.status == 2

@@ -1,0 +1,326 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Bars: fp32 inputs -> max relative error 1e-4 (|g-r| / max(|r|, 1e-2)); bf16 /
+fp8 / int8-KV inputs -> max absolute error 2e-2, plus the internal guards
+normwise error <= 1e-2 and lse error <= 2e-2 (outputs of long-T N(0,1) data are
+small, so the absolute bar alone would be weak).  Both sides read the identical
+stored bytes produced by attn_inputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attn_inputs as gen
+import exact_long_context_tiled_amd as attn
+from util import lse_err, max_abs_err, max_rel_err, normwise_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-4
+LP_TOL = 2e-2
+NORM_TOL = 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def check_lp(o, lse, ro, rlse, what):
+    ea, en, el = max_abs_err(o, ro), normwise_err(o, ro), lse_err(lse, rlse)
+    say(f"{what}: max_abs={ea:.3e} normwise={en:.3e} lse={el:.3e}")
+    assert np.all(np.isfinite(o)), what
+    assert ea <= LP_TOL, what
+    assert en <= NORM_TOL, what
+    assert el <= LP_TOL, what
+
+
+def check_f32(o, lse, ro, rlse, what):
+    er = max_rel_err(o, ro)
+    fin = np.isfinite(rlse)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(rlse)), what
+    el = float(np.max(np.abs(lse[fin] - rlse[fin]) / np.maximum(1.0, np.abs(rlse[fin])))) if fin.any() else 0.0
+    say(f"{what}: max_rel={er:.3e} lse_rel={el:.3e}")
+    assert er <= F32_TOL and el <= F32_TOL, what
+
+
+def gpu_prefill(case, causal=True):
+    q, k, v = (to_dev(case[n]) for n in "qkv")
+    o, lse = attn.prefill(q, k, v, causal=causal, scale=case["scale"])
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), lse.cpu().numpy()
+
+
+# ------------------------------------------------------------------ prefill
+def test_prefill_tiny_gqa_causal_f32():
+    """B=1 Hq=4 Hkv=2 S=T=256 D=64, fp32, scale 1/8, causal: exact to fp32 rounding."""
+    w = gen.WORKLOADS["tiny_gqa_causal_f32"]
+    case = gen.prefill_inputs(w["B"], w["Hq"], w["Hkv"], w["S"], w["T"], w["D"], kind="f32", seed=0x5EED + 1)
+    assert case["scale"] == 1 / 8
+    o, lse = gpu_prefill(case)
+    import oracle
+    ro, rl = oracle.prefill(case)
+    check_f32(o, lse, ro, rl, "tiny f32")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,T,D,causal", [
+    (2, 6, 3, 77, 133, 128, True), (1, 4, 4, 200, 200, 64, False), (1, 2, 1, 300, 40, 64, True),
+    (1, 5, 5, 1, 97, 128, True)])
+def test_prefill_f32_shapes(B, Hq, Hkv, S, T, D, causal):
+    case = gen.prefill_inputs(B, Hq, Hkv, S, T, D, kind="f32", seed=3 + S + T)
+    o, lse = gpu_prefill(case, causal)
+    import oracle
+    ro, rl = oracle.prefill(case, causal=causal)
+    check_f32(o, lse, ro, rl, f"f32 {B,Hq,Hkv,S,T,D,causal}")
+
+
+BF16_SHAPES = [
+    (1, 4, 2, 256, 256, 64, True),     # several tiles, D=64
+    (2, 10, 2, 300, 300, 128, True),   # G = 5, ragged tails
+    (1, 8, 8, 130, 70, 128, False),    # MHA, non-causal, T < S
+    (2, 40, 8, 200, 333, 128, True),   # LLaMa-13B heads, S != T (bottom-right)
+    (1, 4, 1, 129, 1000, 64, True),    # G = 4, long keys
+    (1, 2, 2, 1, 555, 128, True),      # one query row
+    (1, 6, 2, 40, 90, 128, True),      # S < one tile
+    (1, 3, 1, 150, 20, 128, True),     # S > T: leading rows fully masked
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,T,D,causal", BF16_SHAPES)
+def test_prefill_bf16_shapes(B, Hq, Hkv, S, T, D, causal):
+    case = gen.prefill_inputs(B, Hq, Hkv, S, T, D, kind="bf16", seed=11 + S * 3 + T)
+    o, lse = gpu_prefill(case, causal)
+    import oracle
+    ro, rl = oracle.prefill(case, causal=causal)
+    if causal and S > T:
+        dead = S - T
+        assert np.all(o[:, :dead] == 0) and np.all(np.isneginf(lse[:, :, :dead]))
+    check_lp(o, lse, ro, rl, f"bf16 {B,Hq,Hkv,S,T,D,causal}")
+
+
+def test_prefill_empty_keys():
+    case = gen.prefill_inputs(1, 4, 2, 10, 0, 128, kind="bf16", seed=5)
+    o, lse = gpu_prefill(case, True)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def test_prefill_peaked_and_needle_variants():
+    """Diagnostic inputs with O(1) outputs: Q scaled by 4 (peaked softmax) and
+    planted 'needle' keys equal to a query row (one dominant key per row)."""
+    import oracle
+    case = gen.prefill_inputs(1, 8, 2, 333, 333, 128, kind="bf16", seed=77)
+    q4 = case["q"].copy()
+    # multiply bf16 values by 4 exactly: add 2 to the exponent field of non-zero finite values
+    exp = (q4 >> 7) & 0xFF
+    ok = (exp > 0) & (exp < 250)
+    q4[ok] = q4[ok] + (2 << 7)
+    c4 = dict(case, q=q4)
+    o, lse = gpu_prefill(c4)
+    ro, rl = oracle.prefill(c4)
+    check_lp(o, lse, ro, rl, "peaked q*4")
+    assert np.abs(ro).max() > 0.5
+    # needles: key j := query row j of head 0 of its group, scaled up (a dominant diagonal)
+    k = case["k"].copy()
+    for j in range(0, 333, 7):
+        k[0, j, :, :] = q4[0, j, ::4, :]
+    cn = dict(case, q=q4, k=k)
+    o, lse = gpu_prefill(cn)
+    ro, rl = oracle.prefill(cn)
+    check_lp(o, lse, ro, rl, "needles")
+
+
+def test_prefill_llama13b_full_size_sampled_rows():
+    """B=4 Hq=40 Hkv=8 S=T=4096 D=128 bf16 causal; the oracle on 64 sampled rows x all heads."""
+    import oracle
+    w = gen.WORKLOADS["llama13b_gqa_causal_bf16"]
+    case = gen.prefill_inputs(w["B"], w["Hq"], w["Hkv"], w["S"], w["T"], w["D"], kind="bf16", seed=0x5EED + 2)
+    o, lse = gpu_prefill(case)
+    rows = gen.sample_rows(w["S"], 64, 0x5EED + 2)
+    ro, rl = oracle.prefill(case, rows=rows)
+    check_lp(o[:, rows], lse[:, :, rows], ro, rl, "llama13b sampled")
+    # every output finite, every lse finite (causal S == T: every row sees key 0)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+def test_prefill_deterministic():
+    case = gen.prefill_inputs(2, 10, 2, 300, 300, 128, kind="bf16", seed=9)
+    o1, l1 = gpu_prefill(case)
+    o2, l2 = gpu_prefill(case)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_gqa_equals_mha_with_repeated_kv_on_gpu():
+    case = gen.prefill_inputs(1, 8, 2, 150, 150, 128, kind="bf16", seed=19)
+    o1, l1 = gpu_prefill(case)
+    rep = dict(case, k=np.repeat(case["k"], 4, axis=2), v=np.repeat(case["v"], 4, axis=2), Hkv=8)
+    o2, l2 = gpu_prefill(rep)
+    assert max_abs_err(o1, o2) <= 1e-6 and lse_err(l1, l2) <= 1e-6
+
+
+# ------------------------------------------------------------------ decode
+def gpu_decode(case, num_splits=0):
+    q = to_dev(case["q"])
+    kind = case["kv"]
+    k = to_dev(case["k"], kind)
+    v = to_dev(case["v"], kind)
+    ks = to_dev(case["k_scale"]) if case.get("k_scale") is not None else None
+    vs = to_dev(case["v_scale"]) if case.get("v_scale") is not None else None
+    pt = to_dev(case["page_table"]) if case["paged"] else None
+    lens = to_dev(case["lengths"].astype(np.int32))
+    maxlen = int(case["lengths"].max()) if len(case["lengths"]) else 0
+    o, lse = attn.decode_splitkv(q, k, v, lens, maxlen, page_table=pt, k_scale=ks, v_scale=vs,
+                                 kv_dtype="fp8" if kind == "fp8" else None, scale=case["scale"],
+                                 num_splits=num_splits)
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), lse.cpu().numpy()
+
+
+def test_decode_paged_splitkv_bf16_full():
+    """B=8 Hq=32 Hkv=8 D=128, bf16 paged cache (512-token pages, random table), T_b ~ U[1024, 32768]."""
+    import oracle
+    w = gen.WORKLOADS["paged_splitkv_decode_bf16"]
+    seed = 0x5EED + 3
+    lens = gen.ragged_lengths(w["B"], w["lo"], w["hi"], seed)
+    case = gen.decode_inputs(w["B"], w["Hq"], w["Hkv"], w["D"], lens, kv="bf16", page_size=512, seed=seed)
+    o, lse = gpu_decode(case)
+    ro, rl = oracle.decode(case)
+    check_lp(o, lse, ro, rl, f"paged bf16 decode lens={lens.tolist()}")
+
+
+@pytest.mark.parametrize("kv", ["int8", "fp8"])
+@pytest.mark.parametrize("T", [4096, 65536])
+def test_decode_quantised_full(kv, T):
+    """B=4 Hq=32 Hkv=8 D=128, contiguous int8 (per-token-per-head scales) or fp8 e4m3 (per-head scales)."""
+    import oracle
+    w = gen.WORKLOADS["quant_decode"]
+    lens = np.full(w["B"], T, dtype=np.int32)
+    case = gen.decode_inputs(w["B"], w["Hq"], w["Hkv"], w["D"], lens, kv=kv, paged=False,
+                             seed=0x5EED + 4 + (T == 65536))
+    o, lse = gpu_decode(case)
+    ro, rl = oracle.decode(case)
+    check_lp(o, lse, ro, rl, f"{kv} decode T={T}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("paged,page_size", [(True, 16), (True, 512), (False, 0)])
+@pytest.mark.parametrize("G,D", [(1, 128), (4, 64), (5, 128), (8, 128)])
+def test_decode_ragged_edge_cases(kv, paged, page_size, G, D):
+    import oracle
+    Hkv = 2
+    lens = np.array([0, 1, 15, 16, 17, 513, 2000], dtype=np.int32)
+    case = gen.decode_inputs(len(lens), G * Hkv, Hkv, D, lens, kv=kv, page_size=page_size or 512, paged=paged,
+                             spare=3, seed=100 + G + D + page_size)
+    ro, rl = oracle.decode(case)
+    for ns in (0, 1, 3, 1000):
+        o, lse = gpu_decode(case, num_splits=ns)
+        assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+        check_lp(o, lse, ro, rl, f"{kv} paged={paged} ps={page_size} G={G} D={D} splits={ns}")
+
+
+def test_decode_fp8_every_finite_code():
+    """A cache holding every finite e4m3fn byte: the hardware decode must be OCP e4m3fn."""
+    import oracle
+    B, Hq, Hkv, D = 1, 1, 1, 128
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    T = 64
+    k = np.resize(codes, T * D).reshape(1, 1, T, D).astype(np.uint8)
+    v = np.resize(codes[::-1], T * D).reshape(1, 1, T, D).astype(np.uint8)
+    q = gen.f32_to_bf16_bits(np.full((B, Hq, D), 0.01, np.float32))
+    case = {"q": q, "k": k, "v": v, "k_scale": np.array([0.02], np.float32), "v_scale": np.array([0.5], np.float32),
+            "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "lengths": np.array([T], np.int32), "kv": "fp8",
+            "page_table": None, "page_size": T, "paged": False, "scale": 1 / math.sqrt(D)}
+    o, lse = gpu_decode(case)
+    ro, rl = oracle.decode(case)
+    # values reach +-448*0.5: compare relative to the output scale
+    assert normwise_err(o, ro) <= 1e-3 and lse_err(lse, rl) <= 1e-3
+
+
+def test_decode_equals_last_prefill_row():
+    """GPU cross-check: decode of the last query == last row of causal prefill (contiguous bf16)."""
+    S = T = 700
+    case = gen.prefill_inputs(2, 8, 2, S, T, 128, kind="bf16", seed=31)
+    o, lse = gpu_prefill(case)
+    kc = np.ascontiguousarray(case["k"].transpose(0, 2, 1, 3))  # [B, Hkv, T, D]
+    vc = np.ascontiguousarray(case["v"].transpose(0, 2, 1, 3))
+    dcase = {"q": case["q"][:, -1].copy(), "k": kc, "v": vc, "k_scale": None, "v_scale": None, "B": 2, "Hq": 8,
+             "Hkv": 2, "D": 128, "lengths": np.array([T, T], np.int32), "kv": "bf16", "page_table": None,
+             "page_size": T, "paged": False, "scale": case["scale"]}
+    od, ld = gpu_decode(dcase)
+    assert max_abs_err(od, o[:, -1]) <= 5e-3 and lse_err(ld, lse[:, :, -1]) <= 1e-4
+
+
+# ------------------------------------------------------------------ merge
+@pytest.mark.parametrize("n,R,D", [(1, 5, 64), (7, 300, 128), (3, 33, 17), (0, 4, 8)])
+def test_merge_partials(n, R, D):
+    import oracle
+    rng = np.random.default_rng(n * 1000 + R)
+    op = rng.standard_normal((n, R, D)).astype(np.float32)
+    lp = (rng.standard_normal((n, R)) * 5).astype(np.float32)
+    if n >= 3:
+        lp[1, ::3] = -np.inf      # empty partials
+        op[1, ::3] = np.nan       # never read
+        lp[:, 0] = -np.inf        # a fully empty row
+    o, lse = attn.merge_partials(torch.from_numpy(op).cuda(), torch.from_numpy(lp).cuda())
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge(np.nan_to_num(op, nan=0.0), lp)
+    o, lse = o.cpu().numpy(), lse.cpu().numpy()
+    assert max_rel_err(o, ro) <= 1e-5
+    assert lse_err(lse, rl) <= 1e-5
+
+
+# ------------------------------------------------------------------ streaming
+def _pinned(a: np.ndarray):
+    t = torch.empty(a.shape, dtype={np.dtype(np.uint16): torch.int16, np.dtype(np.float32): torch.float32}[a.dtype],
+                    pin_memory=True)
+    t.numpy()[...] = a.view(np.int16) if a.dtype == np.uint16 else a
+    return t.view(torch.bfloat16) if a.dtype == np.uint16 else t
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+def test_stream_budgeted_small(kind):
+    """Streaming under small budgets == oracle, == unbudgeted device run, stable across budgets."""
+    import oracle
+    B, Hq, Hkv, S, T, D = 2, 8, 2, 1000, 1000, 128
+    case = gen.prefill_inputs(B, Hq, Hkv, S, T, D, kind=kind, seed=41)
+    qh, kh, vh = (_pinned(case[n]) for n in "qkv")
+    o_dev, l_dev = gpu_prefill(case)
+    ro, rl = oracle.prefill(case)
+    outs = []
+    for bq, bk in ((256, 128), (384, 200), (1000, 1000), (0, 0)):
+        budget = 1 << 30 if bq == 0 else 64 << 20
+        o, lse, rep = attn.stream_budgeted(qh, kh, vh, causal=True, scale=case["scale"], budget=budget,
+                                           block_q=bq, block_k=bk)
+        o, lse = o.numpy(), lse.numpy()
+        say(f"stream {kind} bq={bq} bk={bk}: {rep}")
+        assert rep["peak_device_bytes"] <= budget
+        if kind == "f32":
+            check_f32(o, lse, ro, rl, f"stream f32 {bq}x{bk}")
+        else:
+            check_lp(o, lse, ro, rl, f"stream bf16 {bq}x{bk}")
+        # f32: merge order only; bf16: P is rounded to bf16 against each key block's own max
+        tol = 1e-5 if kind == "f32" else 2e-3
+        assert max_abs_err(o, o_dev) <= tol and lse_err(lse, l_dev) <= 1e-4
+        outs.append(o)
+    o_again, _, _ = attn.stream_budgeted(qh, kh, vh, causal=True, scale=case["scale"], budget=64 << 20,
+                                         block_q=256, block_k=128)
+    assert np.array_equal(o_again.numpy(), outs[0])
+
+
+def test_stream_rejects_pageable_host_memory():
+    case = gen.prefill_inputs(1, 4, 2, 64, 64, 64, kind="bf16", seed=3)
+    q = torch.from_numpy(case["q"].view(np.int16)).view(torch.bfloat16)  # pageable
+    k = _pinned(case["k"])
+    v = _pinned(case["v"])
+    with pytest.raises(attn.AttnError) as e:
+        attn.stream_budgeted(q, k, v, causal=True, budget=1 << 30)
+    assert e.value.status == 1 and "pinned" in str(e.value)
+
+
+def test_stream_budget_too_small_fails_before_allocating():
+    case = gen.prefill_inputs(1, 4, 2, 64, 64, 64, kind="bf16", seed=3)
+    qh, kh, vh = (_pinned(case[n]) for n in "qkv")
+    free0 = torch.cuda.mem_get_info()[0]
+    with pytest.raises(attn.AttnError) as e:
+        attn.stream_budgeted(qh, kh, vh, causal=True, budget=4096)
+    assert e.value.status == 3
+    assert torch.cuda.mem_get_info()[0] == free0

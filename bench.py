@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Throughput of the exact-attention hot path on one MI355X.
+
+Headline (``value``): causal GQA prefill in TFLOP/s on the LLaMa-13B-shaped
+workload (B=4, Hq=40, Hkv=8, S=T=4096, D=128, bf16 in, fp32 out), counting
+only unmasked (query, key) pairs at 4*D flop each.  Beside it, in the same run:
+  * ``decode``: split-KV decode over the paged bf16 cache (B=8, Hq=32, Hkv=8,
+    D=128, 512-token pages, ragged lengths U[1024, 32768]) in GB/s of KV bytes
+    of valid tokens (+ q, o, lse), with the cache copies rotated so each
+    timed launch streams from HBM rather than from the 256 MB last-level cache;
+  * ``roofline`` / ``decode.roofline``: achieved vs MI355X peak, timed with HIP
+    events on the stream the kernels are launched on;
+  * ``cpu_baseline``: the fp64 oracle on a bounded sample of query rows of the
+    same prefill workload, on this host's cores.
+``--stream`` adds one run of the budgeted streaming prefill (B=1, Hq=32, Hkv=8,
+S=T=2^20, D=128, bf16, 4 GB device budget) from pinned host memory.
+
+Prints ONE JSON line.  Inputs are seeded synthetic N(0,1) data.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s (prefill) + decode KV GB/s, as fraction of MI355X peak"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk (dense, published 2.5 PF)
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def causal_pairs(S, T):
+    """Number of (query, key) pairs visible under bottom-right causal masking."""
+    tot = 0
+    for i in range(S):
+        tot += max(0, min(T, i + T - S + 1))
+    return tot
+
+
+def timed(fn, steps, warmup, stream):
+    import torch
+
+    for _ in range(warmup):
+        fn(-1)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(steps):
+        fn(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps  # ms per launch
+
+
+def bf16_dev(a):
+    import numpy as np
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bench_prefill(args):
+    import torch
+
+    import attn_inputs as gen
+    import exact_long_context_tiled_amd as attn
+
+    w = gen.WORKLOADS["llama13b_gqa_causal_bf16"]
+    case = gen.prefill_inputs(w["B"], w["Hq"], w["Hkv"], w["S"], w["T"], w["D"], kind="bf16", seed=0x5EED + 2)
+    q, k, v = bf16_dev(case["q"]), bf16_dev(case["k"]), bf16_dev(case["v"])
+    o = torch.empty((w["B"], w["S"], w["Hq"], w["D"]), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w["B"], w["Hq"], w["S"]), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(_):
+        attn.prefill(q, k, v, causal=True, scale=case["scale"], out=o, lse=lse)
+
+    ms = timed(step, args.steps, args.warmup, stream)
+    flops = 4.0 * w["D"] * w["B"] * w["Hq"] * causal_pairs(w["S"], w["T"])
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"prefill: {ms:.4f} ms/launch, {tflops:.1f} TFLOP/s ({flops:.4e} flop)")
+    return case, w, ms, flops, tflops
+
+
+def bench_decode(args):
+    import numpy as np
+    import torch
+
+    import attn_inputs as gen
+    import exact_long_context_tiled_amd as attn
+
+    w = gen.WORKLOADS["paged_splitkv_decode_bf16"]
+    seed = 0x5EED + 3
+    lens = gen.ragged_lengths(w["B"], w["lo"], w["hi"], seed)
+    case = gen.decode_inputs(w["B"], w["Hq"], w["Hkv"], w["D"], lens, kv="bf16", page_size=w["page_size"], seed=seed)
+    q = bf16_dev(case["q"])
+    kc, vc = bf16_dev(case["k"]), bf16_dev(case["v"])
+    pt = torch.from_numpy(case["page_table"]).cuda()
+    lens_d = torch.from_numpy(lens.astype(np.int32)).cuda()
+    maxlen = int(lens.max())
+    valid_tokens = int(lens.sum())
+    kv_bytes = valid_tokens * w["Hkv"] * w["D"] * 2 * 2
+    io_bytes = w["B"] * w["Hq"] * w["D"] * (2 + 4) + w["B"] * w["Hq"] * 4
+    nbytes = kv_bytes + io_bytes
+    cache_bytes = kc.numel() * 2 * 2
+    copies = max(2, math.ceil((1 << 30) / cache_bytes))
+    caches = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(copies - 1)]
+    ws = torch.empty(attn.decode_workspace_size(w["B"], w["Hq"], w["Hkv"], w["D"], maxlen), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty((w["B"], w["Hq"], w["D"]), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w["B"], w["Hq"]), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kk, vv = caches[i % copies]
+        attn.decode_splitkv(q, kk, vv, lens_d, maxlen, page_table=pt, scale=case["scale"], workspace=ws, out=o,
+                            lse=lse)
+
+    steps = max(args.steps, copies * 4)
+    ms = timed(step, steps, max(args.warmup, copies), stream)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"decode: {ms * 1e3:.2f} us/call, {gbs:.1f} GB/s ({nbytes / 1e6:.1f} MB, {copies} cache copies)")
+    return {"workload": "paged_splitkv_decode_bf16", "value": round(gbs, 2), "unit": "GB/s", "us_per_call":
+            round(ms * 1e3, 3), "bytes": nbytes, "valid_tokens": valid_tokens, "lengths": lens.tolist(),
+            "cache_copies": copies, "steps": steps,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+
+
+def cpu_baseline(case, w, target_s):
+    import oracle
+    import attn_inputs as gen
+
+    S, T = w["S"], w["T"]
+
+    def run(n):
+        rows = gen.sample_rows(S, n, 0x5EED + 7)
+        t0 = time.perf_counter()
+        oracle.prefill(case, rows=rows)
+        dt = time.perf_counter() - t0
+        pairs = sum(min(T, int(i) + T - S + 1) for i in rows)
+        return dt, 4.0 * w["D"] * w["B"] * w["Hq"] * pairs, rows
+
+    dt, fl, rows = run(4)
+    rate = fl / dt
+    n = int(max(4, min(512, 4 * target_s / max(dt, 1e-3))))
+    dt, fl, rows = run(n)
+    return {"value": round(fl / dt / 1e12, 8), "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"{len(rows)} seeded query rows (incl. 0 and S-1) x all {w['Hq']} heads x B={w['B']} of the "
+                      f"same prefill workload, fp64 naive softmax, {fl:.3e} flop"}
+
+
+def bench_stream(args):
+    import numpy as np
+    import torch
+
+    import attn_inputs as gen
+    import exact_long_context_tiled_amd as attn
+
+    w = gen.WORKLOADS["stream_cqsa_causal_1m"]
+    B, Hq, Hkv, S, T, D = w["B"], w["Hq"], w["Hkv"], w["S"], w["T"], w["D"]
+    seed = 0x5EED + 5
+    t0 = time.perf_counter()
+    hq = torch.empty((B, S, Hq, D), dtype=torch.int16, pin_memory=True)
+    hk = torch.empty((B, T, Hkv, D), dtype=torch.int16, pin_memory=True)
+    hv = torch.empty((B, T, Hkv, D), dtype=torch.int16, pin_memory=True)
+    gen.normal(hq.shape, seed, gen.TID_Q, "bf16", out=hq.numpy().view(np.uint16))
+    gen.normal(hk.shape, seed, gen.TID_K, "bf16", out=hk.numpy().view(np.uint16))
+    gen.normal(hv.shape, seed, gen.TID_V, "bf16", out=hv.numpy().view(np.uint16))
+    log(f"stream: inputs generated in {time.perf_counter() - t0:.1f} s")
+    o, lse, rep = attn.stream_budgeted(hq.view(torch.bfloat16), hk.view(torch.bfloat16), hv.view(torch.bfloat16),
+                                       causal=True, scale=1 / math.sqrt(D), budget=w["budget"])
+    flops = 4.0 * D * B * Hq * (S * (S + 1) // 2)
+    log(f"stream: {rep}")
+    return {"workload": "stream_cqsa_causal_1m", "budget_bytes": w["budget"], "report": rep,
+            "tflops_end_to_end": round(flops / rep["wall_s"] / 1e12, 2),
+            "tflops_kernels": round(flops / rep["kernel_s"] / 1e12, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--stream", action="store_true", help="also run the 2^20-token budgeted streaming workload")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (sharding is a design note only); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs an MI355X"
+    torch.cuda.set_device(0)
+    case, w, ms, flops, tflops = bench_prefill(args)
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1), bf16)",
+        "config": {"workload": "llama13b_gqa_causal_bf16", "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"],
+                   "S": w["S"], "T": w["T"], "D": w["D"], "causal": True, "flop_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_decode:
+        out["decode"] = bench_decode(args)
+    if args.stream:
+        out["stream"] = bench_stream(args)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(case, w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

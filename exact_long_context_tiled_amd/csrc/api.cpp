@@ -149,7 +149,6 @@ extern "C" attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, cons
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.chunk = plan.chunk;
-  a.sub_chunk = plan.sub_chunk;
   a.n_splits = plan.n_splits;
   a.scale_log2 = scale * kLog2e;
   const size_t rows = (size_t)plan.n_splits * (size_t)B * (size_t)Hq;

@@ -69,7 +69,6 @@ struct DecodeArgs {
   const int32_t* kv_lens;
   int B, Hq, Hkv;
   int chunk;     // tokens per split (multiple of 16)
-  int sub_chunk; // tokens scored into LDS at once (multiple of 16, <= chunk)
   int n_splits;  // splits per sequence in the grid
   float scale_log2;
   float* part_o;    // [n_splits, B*Hq, D]
@@ -78,7 +77,6 @@ struct DecodeArgs {
 
 struct DecodePlan {
   int chunk;
-  int sub_chunk;
   int n_splits;
 };
 DecodePlan plan_decode(int B, int Hq, int Hkv, int max_kv_len, int num_splits);

@@ -11,14 +11,17 @@
 // "Methodology" item 1, ONNX Runtime PR #28695 analysis, section 1); bytes are
 // dequantised in registers right after the 16-byte loads.
 //
-// This is a bandwidth-bound scan, so the vector ALUs do the arithmetic: the
-// lanes of a wave are split into token slots of D*bytes/16 lanes, each lane
-// owning one 16-byte slice of a K (then V) row.
-//   pass 1: scores s[t][g] = scale * q_g . k_t  (slice dot + lane reduction)
-//           into LDS;
-//   stats : per head the chunk max m_g and sum l_g of exp(s - m_g);
-//   pass 2: acc_g += p[t][g] * v_t over the chunk, then a reduction over
-//           token slots and waves.
+// This is a bandwidth-bound scan, so the vector ALUs do the arithmetic.  The
+// lanes of a wave form token slots of D*bytes/16 lanes, each lane owning one
+// 16-byte slice of a token's K and V rows; every iteration a wave loads the K
+// and V slices of 4 tokens per slot (all loads in flight together), reduces
+// the slice dot products across the slot with row-local DPP moves, and
+// folds the tokens into a per-slot online softmax (running max, sum and
+// output accumulator).  bf16 K is dotted with the exact bf16 query in packed
+// bf16 pairs; int8 / fp8 slices are converted to fp32.  At the end the slots
+// of a wave, then the four waves, are combined by the same max/rescale rule.
+// Pages hold >= 16 tokens, so the page-table entry of each load step is one
+// wave-uniform (scalar) read.
 #include <math.h>
 
 #include <algorithm>
@@ -27,8 +30,6 @@
 
 namespace attn {
 namespace {
-
-constexpr int kMaxChunkScores = 8192;  // chunk * G floats of scores in LDS
 
 template <int KV>
 struct KvTraits;
@@ -84,17 +85,30 @@ __device__ __forceinline__ int64_t cache_row(const DecodeArgs& a, int b, int hk,
   return ((int64_t)b * a.Hkv + hk) * a.page_size + t;
 }
 
+// Sum over the LPT lanes (1, 2, 4, 8 or 16 adjacent lanes) that hold one
+// token's slices, with row-local DPP moves (no LDS round trip).
+template <int LPT>
+__device__ __forceinline__ float token_sum(float x) {
+  if constexpr (LPT >= 2) x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, false));  // xor 1
+  if constexpr (LPT >= 4) x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xf, 0xf, false));  // xor 2
+  if constexpr (LPT >= 8) x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xf, 0xf, false));  // mirror in 8
+  if constexpr (LPT >= 16) x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xf, 0xf, false));  // mirror in 16
+  return x;
+}
+
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
 template <int KV, int D, int G>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   constexpr int EB = KvTraits<KV>::kBytes;
-  constexpr int EPL = 16 / EB;     // elements per lane slice
-  constexpr int LPT = D / EPL;     // lanes per token
-  constexpr int TPW = 64 / LPT;    // tokens per wave step
-  constexpr int TPB = 4 * TPW;     // tokens per work-group step
-  constexpr int U = 4;             // steps unrolled (loads in flight)
-  extern __shared__ float smem[];
-  float* sc = smem;  // [sub_chunk][G]; reused for the final reduction
-  __shared__ float stat_m[G], stat_l[G], stat_a[G];
+  constexpr int EPL = 16 / EB;   // elements per lane slice
+  constexpr int LPT = D / EPL;   // lanes per token
+  constexpr int TPW = 64 / LPT;  // tokens per wave per load step (token slots)
+  constexpr int U = 4;           // load steps per iteration
+  constexpr int TPI = TPW * U;   // tokens per wave per iteration
+  constexpr bool kDot2 = KV == ATTN_BF16;
+  __shared__ float red_acc[4][G * D];
+  __shared__ float red_m[4][G], red_l[4][G];
 
   const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -108,184 +122,191 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
     if (tid < G) a.part_lse[(int64_t)split * BHq + row0 + tid] = -INFINITY;
     return;
   }
-  if (tid < G) {
-    stat_m[tid] = -INFINITY;
-    stat_l[tid] = 0.f;
-  }
 
-  // query slice, pre-multiplied by scale*log2(e) (and the fp8 K scale)
-  float qs[G][EPL];
+  // query slices: exact bf16 pairs for the packed dot (bf16 cache), or fp32
+  // pre-multiplied by scale*log2(e) (and the fp8 per-head K scale)
+  bf16x2 q2[kDot2 ? G : 1][kDot2 ? EPL / 2 : 1];
+  float qf[kDot2 ? 1 : G][kDot2 ? 1 : EPL];
+  float smul = a.scale_log2;
   {
-    float qmul = a.scale_log2;
-    if constexpr (KV == ATTN_FP8_E4M3) qmul *= a.k_scale[hk];
     const uint16_t* qb = (const uint16_t*)a.q + row0 * D + part * EPL;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
       for (int e = 0; e < EPL; e += 8) {
         const uint4 raw = *(const uint4*)(qb + (int64_t)g * D + e);
-        float tmp[8];
-        decode16<ATTN_BF16>(raw, tmp);
+        if constexpr (kDot2) {
+          const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) qs[g][e + i] = tmp[i] * qmul;
+          for (int i = 0; i < 4; ++i) q2[g][e / 2 + i] = __builtin_bit_cast(bf16x2, wd[i]);
+        } else {
+          float tmp[8];
+          decode16<ATTN_BF16>(raw, tmp);
+          float qmul = a.scale_log2;
+          if constexpr (KV == ATTN_FP8_E4M3) qmul *= a.k_scale[hk];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) qf[g][e + i] = tmp[i] * qmul;
+        }
       }
     }
+    if constexpr (!kDot2) smul = 1.f;
+  }
+
+  float m[G], l[G], acc[G][EPL];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
   }
 
   const uint8_t* kb = (const uint8_t*)a.k;
   const uint8_t* vb = (const uint8_t*)a.v;
-  const int my_off = w * TPW + slot;
-  const int sub = a.sub_chunk;  // tokens whose scores fit in LDS at once
+  const int64_t lane_off = (int64_t)part * EPL * EB;
 
-  float acc[G][EPL];
+  for (int g0 = t0 + w * TPI; g0 < t1; g0 += 4 * TPI) {
+    uint4 kr[U], vr[U];
+    float ksc[U], vsc[U];
+    bool ok[U];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
-
-  // A chunk longer than `sub` is scanned in sub-chunks with an online
-  // rescale of the running (max, sum, accumulator) between them.
-  for (int s0 = t0; s0 < t1; s0 += sub) {
-    const int s1 = min(t1, s0 + sub);
-    const int ns = s1 - s0;
-    // ---------------- pass 1: scores
-    for (int tb = s0; tb < s1; tb += U * TPB) {
-      uint4 raw[U];
-      int64_t crow[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = tb + u * TPB + my_off;
-        raw[u] = uint4{0, 0, 0, 0};
-        crow[u] = 0;
-        if (t < s1) {
-          crow[u] = cache_row(a, b, hk, t);
-          raw[u] = *(const uint4*)(kb + (crow[u] * D + part * EPL) * EB);
+    for (int u = 0; u < U; ++u) {
+      // TPW consecutive tokens starting at a TPW-aligned index never straddle a page
+      const int tstep = g0 + u * TPW;  // wave-uniform
+      const int t = tstep + slot;
+      int64_t rowbase;
+      if (a.page_table) {
+        // only steps that start inside the sequence read the table (its later entries may not exist)
+        const int pg = tstep < t1 ? a.page_table[(int64_t)b * a.max_pages + (tstep >> a.page_shift)] : 0;
+        rowbase = ((int64_t)pg * a.Hkv + hk) * a.page_size - (tstep & ~(a.page_size - 1));
+      } else {
+        rowbase = ((int64_t)b * a.Hkv + hk) * a.page_size;
+      }
+      const int64_t row = rowbase + t;
+      ok[u] = t < t1;
+      kr[u] = vr[u] = uint4{0, 0, 0, 0};
+      ksc[u] = vsc[u] = 1.f;
+      if (ok[u]) {
+        kr[u] = *(const uint4*)(kb + row * (D * EB) + lane_off);
+        vr[u] = *(const uint4*)(vb + row * (D * EB) + lane_off);
+        if constexpr (KV == ATTN_INT8) {
+          ksc[u] = a.k_scale[row];  // q already carries scale*log2(e)
+          vsc[u] = a.v_scale[row];
         }
       }
+    }
+    // scores of the U tokens of this lane's slot, in the log2 domain
+    float s[U][G];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = tb + u * TPB + my_off;
-        float kv[EPL];
-        decode16<KV>(raw[u], kv);
-        float dot[G];
+    for (int u = 0; u < U; ++u) {
+      if constexpr (kDot2) {
+        const uint32_t wd[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          float acc_s = 0.f;
+          float d = 0.f;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc_s = fmaf(qs[g][e], kv[e], acc_s);
-          dot[g] = acc_s;
+          for (int i = 0; i < 4; ++i) d = __builtin_amdgcn_fdot2_f32_bf16(q2[g][i], __builtin_bit_cast(bf16x2, wd[i]), d, false);
+          s[u][g] = d;
         }
+      } else {
+        float kv[EPL];
+        decode16<KV>(kr[u], kv);
 #pragma unroll
-        for (int off = 1; off < LPT; off <<= 1) {
+        for (int g = 0; g < G; ++g) {
+          float d = 0.f;
 #pragma unroll
-          for (int g = 0; g < G; ++g) dot[g] += __shfl_xor(dot[g], off);
+          for (int e = 0; e < EPL; ++e) d = fmaf(qf[g][e], kv[e], d);
+          s[u][g] = d;
         }
-        if (part == 0 && t < s1) {
-          float ks = 1.f;
-          if constexpr (KV == ATTN_INT8) ks = a.k_scale[crow[u]];
+      }
 #pragma unroll
-          for (int g = 0; g < G; ++g) sc[(t - s0) * G + g] = dot[g] * ks;
-        }
+      for (int g = 0; g < G; ++g) {
+        const float x = token_sum<LPT>(s[u][g]) * (KV == ATTN_INT8 ? ksc[u] : smul);
+        s[u][g] = ok[u] ? x : -INFINITY;
       }
     }
-    __syncthreads();
-
-    // ---------------- softmax statistics of the sub-chunk, one wave per head
-    for (int g = w; g < G; g += 4) {
-      float mx = -INFINITY;
-      for (int i = lane; i < ns; i += 64) mx = fmaxf(mx, sc[i * G + g]);
+    // online softmax over the slot's tokens, then accumulate P.V
+    float vv[U][EPL];
 #pragma unroll
-      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-      const float m_old = stat_m[g];  // -inf before the first sub-chunk
-      const float m_new = fmaxf(m_old, mx);
-      float sum = 0.f;
-      for (int i = lane; i < ns; i += 64) {
-        const float p = __builtin_amdgcn_exp2f(sc[i * G + g] - m_new);
-        sc[i * G + g] = p;
-        sum += p;
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
-      if (lane == 0) {
-        const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);
-        stat_a[g] = alpha;
-        stat_l[g] = stat_l[g] * alpha + sum;
-        stat_m[g] = m_new;
-      }
-    }
-    __syncthreads();
-
-    // ---------------- pass 2: P.V
+    for (int u = 0; u < U; ++u) decode16<KV>(vr[u], vv[u]);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const float alpha = stat_a[g];
+      float mx = s[0][g];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
-    }
-    for (int tb = s0; tb < s1; tb += U * TPB) {
-      uint4 raw[U];
-      int64_t crow[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int t = tb + u * TPB + my_off;
-        raw[u] = uint4{0, 0, 0, 0};
-        crow[u] = 0;
-        if (t < s1) {
-          crow[u] = cache_row(a, b, hk, t);
-          raw[u] = *(const uint4*)(vb + (crow[u] * D + part * EPL) * EB);
-        }
-      }
+      for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][g]);
+      const float m_new = fmaxf(m[g], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m[g] - m_use);
+      m[g] = m_new;
+      float lsum = 0.f;
+      float p[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int t = tb + u * TPB + my_off;
-        if (t < s1) {
-          float vv[EPL];
-          decode16<KV>(raw[u], vv);
-          float vsc = 1.f;
-          if constexpr (KV == ATTN_INT8) vsc = a.v_scale[crow[u]];
+        p[u] = __builtin_amdgcn_exp2f(s[u][g] - m_use);
+        lsum += p[u];
+        if constexpr (KV == ATTN_INT8) p[u] *= vsc[u];
+      }
+      l[g] = l[g] * alpha + lsum;
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            const float p = sc[(t - s0) * G + g] * vsc;
+      for (int e = 0; e < EPL; ++e) {
+        float x = acc[g][e] * alpha;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) acc[g][e] = fmaf(p, vv[e], acc[g][e]);
-          }
-        }
+        for (int u = 0; u < U; ++u) x = fmaf(p[u], vv[u][e], x);
+        acc[g][e] = x;
       }
     }
-    __syncthreads();  // sc is rewritten by the next sub-chunk
   }
-  // reduce over the token slots of the wave (lanes with equal `part`)
+
+  // combine the token slots of the wave (lanes 16/32 apart hold the same d slice)
 #pragma unroll
   for (int off = LPT; off < 64; off <<= 1) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
+      const float mo = __shfl_xor(m[g], off);
+      const float lo = __shfl_xor(l[g], off);
+      const float M = fmaxf(m[g], mo);
+      const float Mu = M == -INFINITY ? 0.f : M;
+      const float fs = __builtin_amdgcn_exp2f(m[g] - Mu), fo = __builtin_amdgcn_exp2f(mo - Mu);
+      l[g] = l[g] * fs + lo * fo;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] += __shfl_xor(acc[g][e], off);
+      for (int e = 0; e < EPL; ++e) acc[g][e] = acc[g][e] * fs + __shfl_xor(acc[g][e], off) * fo;
+      m[g] = M;
+    }
   }
-  float* red = smem;  // [4][G*D]; the last sub-chunk's scores are dead
+  // combine the four waves through LDS
   if (slot == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) red[w * G * D + g * D + part * EPL + e] = acc[g][e];
+      for (int e = 0; e < EPL; ++e) red_acc[w][g * D + part * EPL + e] = acc[g][e];
+      if (part == 0) {
+        red_m[w][g] = m[g];
+        red_l[w][g] = l[g];
+      }
+    }
   }
   __syncthreads();
   float vmul = 1.f;
   if constexpr (KV == ATTN_FP8_E4M3) vmul = a.v_scale[hk];
   for (int idx = tid; idx < G * D; idx += 256) {
     const int g = idx / D;
-    const float s = red[idx] + red[G * D + idx] + red[2 * G * D + idx] + red[3 * G * D + idx];
-    a.part_o[((int64_t)split * BHq + row0 + g) * D + (idx - g * D)] = s * (vmul / stat_l[g]);
+    const float M = fmaxf(fmaxf(red_m[0][g], red_m[1][g]), fmaxf(red_m[2][g], red_m[3][g]));
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float f = red_m[ww][g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[ww][g] - M);
+      num = fmaf(f, red_acc[ww][idx], num);
+      den = fmaf(f, red_l[ww][g], den);
+    }
+    a.part_o[((int64_t)split * BHq + row0 + g) * D + (idx - g * D)] = num * (vmul / den);
+    if (idx - g * D == 0) a.part_lse[(int64_t)split * BHq + row0 + g] = (M + __log2f(den)) * kLn2;
   }
-  if (tid < G)
-    a.part_lse[(int64_t)split * BHq + row0 + tid] = (stat_m[tid] + __log2f(stat_l[tid])) * kLn2;
 }
 
 template <int KV, int D, int G>
 attn_status launch_one(const DecodeArgs& a, hipStream_t stream) {
-  const size_t smem = sizeof(float) * (size_t)std::max(a.sub_chunk * G, 4 * G * D);
   dim3 grid(a.n_splits, a.Hkv, a.B);
-  hipLaunchKernelGGL((decode_split_kernel<KV, D, G>), grid, dim3(256), smem, stream, a);
+  hipLaunchKernelGGL((decode_split_kernel<KV, D, G>), grid, dim3(256), 0, stream, a);
   return check_launch("decode_split");
 }
 
@@ -313,7 +334,6 @@ attn_status launch_d(const DecodeArgs& a, int D, int G, hipStream_t stream) {
 
 DecodePlan plan_decode(int B, int Hq, int Hkv, int max_kv_len, int num_splits) {
   DecodePlan p;
-  const int G = Hkv > 0 ? std::max(Hq / Hkv, 1) : 1;
   int chunk;
   if (max_kv_len <= 0) {
     chunk = 16;
@@ -332,7 +352,6 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int max_kv_len, int num_splits) {
   }
   chunk = (chunk + 15) / 16 * 16;
   p.chunk = chunk;
-  p.sub_chunk = std::min(chunk, std::max(16, kMaxChunkScores / G / 16 * 16));
   p.n_splits = max_kv_len <= 0 ? 1 : (max_kv_len + chunk - 1) / chunk;
   return p;
 }

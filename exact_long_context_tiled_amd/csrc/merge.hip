@@ -3,9 +3,6 @@
 // exact recombination of independent sub-results: Stream-CQSA summary,
 // "Methodology" item 2).
 //
-// One wave per output row: every lane reads the n partial lse values (the same
-// addresses, served as one broadcast), forms the weights, then streams its
-// share of the D columns of every non-empty partial.
 #include <math.h>
 
 #include "common.h"
@@ -13,33 +10,93 @@
 namespace attn {
 namespace {
 
+__device__ __forceinline__ float block_max(float x, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ float block_sum(float x, float* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// One work-group per output row.  The partials' weights are formed once per
+// chunk of 256 partials in LDS; the columns are then accumulated by
+// 256 / D thread groups in parallel (each over a strided subset of the
+// partials) and the groups are summed at the end.
 __global__ void __launch_bounds__(256) merge_kernel(int n, const float* __restrict__ op,
                                                     const float* __restrict__ lp, int64_t R, int D,
                                                     float* __restrict__ o, float* __restrict__ lse) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= R) return;
-  float M = -INFINITY;
-  for (int c = 0; c < n; ++c) M = fmaxf(M, lp[(int64_t)c * R + row]);
+  __shared__ float wts[256];
+  __shared__ float red[4];
+  __shared__ float part[256];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  float mx = -INFINITY;
+  for (int c = tid; c < n; c += 256) mx = fmaxf(mx, lp[(int64_t)c * R + row]);
+  mx = block_max(mx, red);
   float* orow = o + row * D;
-  if (M == -INFINITY) {
-    for (int d = lane; d < D; d += 64) orow[d] = 0.f;
-    if (lane == 0 && lse) lse[row] = -INFINITY;
+  if (mx == -INFINITY) {  // no partial holds a key
+    for (int d = tid; d < D; d += 256) orow[d] = 0.f;
+    if (tid == 0 && lse) lse[row] = -INFINITY;
     return;
   }
+  const int ng = D >= 256 ? 1 : 256 / D;      // column groups working on disjoint partials
+  const int grp = D >= 256 ? 0 : tid / D;
+  const int dl = D >= 256 ? tid : tid % D;
+  const bool active = grp < ng;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};  // D <= 1024 -> at most 4 columns per thread
   float den = 0.f;
-  for (int c = 0; c < n; ++c) den += expf(lp[(int64_t)c * R + row] - M);
-  const float inv = 1.f / den;
-  for (int d = lane; d < D; d += 64) {
-    float acc = 0.f;
-    for (int c = 0; c < n; ++c) {
-      const float lc = lp[(int64_t)c * R + row];
-      if (lc == -INFINITY) continue;  // empty partial: its O is never read
-      acc = fmaf(expf(lc - M), op[((int64_t)c * R + row) * D + d], acc);
+  for (int c0 = 0; c0 < n; c0 += 256) {
+    __syncthreads();
+    float wv = 0.f;
+    if (c0 + tid < n) {
+      const float lc = lp[(int64_t)(c0 + tid) * R + row];
+      wv = lc == -INFINITY ? 0.f : expf(lc - mx);  // an empty partial's O is never read
     }
-    orow[d] = acc * inv;
+    wts[tid] = wv;
+    den += wv;
+    __syncthreads();
+    const int cend = min(256, n - c0);
+    if (active) {
+      for (int c = grp; c < cend; c += ng) {
+        const float wc = wts[c];
+        if (wc == 0.f) continue;
+        const float* src = op + ((int64_t)(c0 + c) * R + row) * D;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int d = dl + 256 * k;
+          if (d < D) acc[k] = fmaf(wc, src[d], acc[k]);
+        }
+      }
+    }
   }
-  if (lane == 0 && lse) lse[row] = M + logf(den);
+  den = block_sum(den, red);
+  const float inv = 1.f / den;
+  if (ng > 1) {
+    part[tid] = acc[0];
+    __syncthreads();
+    if (tid < D) {
+      float s = 0.f;
+      for (int g = 0; g < ng; ++g) s += part[g * D + tid];
+      orow[tid] = s * inv;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int d = dl + 256 * k;
+      if (d < D) orow[d] = acc[k] * inv;
+    }
+  }
+  if (tid == 0 && lse) lse[row] = mx + logf(den);
 }
 
 }  // namespace
@@ -47,10 +104,8 @@ __global__ void __launch_bounds__(256) merge_kernel(int n, const float* __restri
 attn_status launch_merge(int n, const float* o_parts, const float* lse_parts, int64_t R, int D, float* o,
                          float* lse, hipStream_t stream) {
   if (R == 0) return ATTN_OK;
-  const int64_t blocks = (R + 3) / 4;
-  if (blocks > 0x7fffffff) return set_error(ATTN_E_UNSUPPORTED, "merge: too many rows");
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, n, o_parts, lse_parts, R, D, o,
-                     lse);
+  if (R > 0x7fffffff) return set_error(ATTN_E_UNSUPPORTED, "merge: too many rows");
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)R), dim3(256), 0, stream, n, o_parts, lse_parts, R, D, o, lse);
   return check_launch("merge");
 }
 

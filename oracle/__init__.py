@@ -54,6 +54,8 @@ def load():
         lib.oracle_e4m3fn_value.restype = ctypes.c_double
         lib.oracle_bf16_value.argtypes = [ctypes.c_uint16]
         lib.oracle_bf16_value.restype = ctypes.c_double
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -127,6 +129,11 @@ def merge(o_parts, lse_parts):
 
 def e4m3fn_value(code: int) -> float:
     return load().oracle_e4m3fn_value(code)
+
+
+def threads() -> int:
+    """OpenMP threads the oracle uses."""
+    return load().oracle_threads()
 
 
 def bf16_value(bits: int) -> float:

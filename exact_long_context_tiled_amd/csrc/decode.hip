@@ -104,7 +104,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   constexpr int EPL = 16 / EB;   // elements per lane slice
   constexpr int LPT = D / EPL;   // lanes per token
   constexpr int TPW = 64 / LPT;  // tokens per wave per load step (token slots)
-  constexpr int U = 4;           // load steps per iteration
+  constexpr int U = EB == 2 ? 4 : 2;  // load steps per iteration (16 tokens per wave at D = 128)
   constexpr int TPI = TPW * U;   // tokens per wave per iteration
   constexpr bool kDot2 = KV == ATTN_BF16;
   __shared__ float red_acc[4][G * D];
@@ -165,42 +165,58 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   const uint8_t* vb = (const uint8_t*)a.v;
   const int64_t lane_off = (int64_t)part * EPL * EB;
 
-  for (int g0 = t0 + w * TPI; g0 < t1; g0 += 4 * TPI) {
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index as a scalar
+  const int64_t hk_rows = (int64_t)hk * a.page_size;
+  constexpr int kStride = 4 * TPI;  // tokens between a wave's consecutive iterations
+
+  // Loads of one iteration (U steps of TPW tokens).  TPW consecutive tokens
+  // from a TPW-aligned index never straddle a page and every step index is
+  // wave-uniform, so the page-table entries are scalar loads issued first.
+  struct Buf {
     uint4 kr[U], vr[U];
     float ksc[U], vsc[U];
-    bool ok[U];
+  };
+  // Every call issues the same number of vector loads with no branch around
+  // them (tokens past the chunk are clamped onto its last token, a cache
+  // hit), so the compiler's wait counters keep the next iteration's loads in
+  // flight while the current one is consumed.
+  auto issue = [&](int g0, Buf& bf) {
+    int64_t step_row[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      // TPW consecutive tokens starting at a TPW-aligned index never straddle a page
-      const int tstep = g0 + u * TPW;  // wave-uniform
-      const int t = tstep + slot;
-      int64_t rowbase;
+      // wave-uniform and inside the sequence; readfirstlane keeps it (and the
+      // page-table read) on the scalar unit, off the vector-load counter
+      const int tc = __builtin_amdgcn_readfirstlane(min(g0 + u * TPW, t1 - 1));
       if (a.page_table) {
-        // only steps that start inside the sequence read the table (its later entries may not exist)
-        const int pg = tstep < t1 ? a.page_table[(int64_t)b * a.max_pages + (tstep >> a.page_shift)] : 0;
-        rowbase = ((int64_t)pg * a.Hkv + hk) * a.page_size - (tstep & ~(a.page_size - 1));
+        // read through the constant address space: a scalar (SMEM) load
+        const auto* pt = (const __attribute__((address_space(4))) int32_t*)a.page_table;
+        const int pg = pt[(int64_t)b * a.max_pages + (tc >> a.page_shift)];
+        step_row[u] = (int64_t)pg * a.Hkv * a.page_size + hk_rows - (tc & ~(a.page_size - 1));
       } else {
-        rowbase = ((int64_t)b * a.Hkv + hk) * a.page_size;
-      }
-      const int64_t row = rowbase + t;
-      ok[u] = t < t1;
-      kr[u] = vr[u] = uint4{0, 0, 0, 0};
-      ksc[u] = vsc[u] = 1.f;
-      if (ok[u]) {
-        kr[u] = *(const uint4*)(kb + row * (D * EB) + lane_off);
-        vr[u] = *(const uint4*)(vb + row * (D * EB) + lane_off);
-        if constexpr (KV == ATTN_INT8) {
-          ksc[u] = a.k_scale[row];  // q already carries scale*log2(e)
-          vsc[u] = a.v_scale[row];
-        }
+        step_row[u] = (int64_t)b * a.Hkv * a.page_size + hk_rows;
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t row = step_row[u] + min(g0 + u * TPW + slot, t1 - 1);
+      bf.kr[u] = *(const uint4*)(kb + row * (D * EB) + lane_off);
+      bf.vr[u] = *(const uint4*)(vb + row * (D * EB) + lane_off);
+      if constexpr (KV == ATTN_INT8) {
+        bf.ksc[u] = a.k_scale[row];  // q already carries scale*log2(e)
+        bf.vsc[u] = a.v_scale[row];
+      } else {
+        bf.ksc[u] = bf.vsc[u] = 1.f;
+      }
+    }
+  };
+  auto consume = [&](int g0, const Buf& bf) {
     // scores of the U tokens of this lane's slot, in the log2 domain
     float s[U][G];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const bool ok = g0 + u * TPW + slot < t1;
       if constexpr (kDot2) {
-        const uint32_t wd[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
+        const uint32_t wd[4] = {bf.kr[u].x, bf.kr[u].y, bf.kr[u].z, bf.kr[u].w};
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           float d = 0.f;
@@ -210,7 +226,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
         }
       } else {
         float kv[EPL];
-        decode16<KV>(kr[u], kv);
+        decode16<KV>(bf.kr[u], kv);
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           float d = 0.f;
@@ -221,14 +237,14 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float x = token_sum<LPT>(s[u][g]) * (KV == ATTN_INT8 ? ksc[u] : smul);
-        s[u][g] = ok[u] ? x : -INFINITY;
+        const float x = token_sum<LPT>(s[u][g]) * (KV == ATTN_INT8 ? bf.ksc[u] : smul);
+        s[u][g] = ok ? x : -INFINITY;
       }
     }
     // online softmax over the slot's tokens, then accumulate P.V
     float vv[U][EPL];
 #pragma unroll
-    for (int u = 0; u < U; ++u) decode16<KV>(vr[u], vv[u]);
+    for (int u = 0; u < U; ++u) decode16<KV>(bf.vr[u], vv[u]);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float mx = s[0][g];
@@ -244,7 +260,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
       for (int u = 0; u < U; ++u) {
         p[u] = __builtin_amdgcn_exp2f(s[u][g] - m_use);
         lsum += p[u];
-        if constexpr (KV == ATTN_INT8) p[u] *= vsc[u];
+        if constexpr (KV == ATTN_INT8) p[u] *= bf.vsc[u];
       }
       l[g] = l[g] * alpha + lsum;
 #pragma unroll
@@ -254,6 +270,29 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
         for (int u = 0; u < U; ++u) x = fmaf(p[u], vv[u][e], x);
         acc[g][e] = x;
       }
+    }
+  };
+
+  // two-stage software pipeline: the next iteration's loads are in flight
+  // while the current one is consumed
+  Buf b0, b1;
+  int g0 = t0 + wu * TPI;
+  // (the scheduling barriers keep the compiler from sinking a batch of loads
+  // down to its consumer to save registers, which would serialise them)
+  if (g0 < t1) {
+    issue(g0, b0);
+    while (true) {
+      const int g1 = g0 + kStride;
+      issue(g1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(g0, b0);
+      if (g1 >= t1) break;
+      const int g2 = g1 + kStride;
+      issue(g2, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(g1, b1);
+      if (g2 >= t1) break;
+      g0 = g2;
     }
   }
 
@@ -344,10 +383,10 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int max_kv_len, int num_splits) {
     if (env && atoi(env) > 0) {
       chunk = atoi(env);
     } else {
-      // enough chunks for ~2048 work-groups, never below 128 tokens each
-      const int64_t target = 2048;
+      // enough chunks for ~4096 work-groups (16 per CU), never below 256 tokens each
+      const int64_t target = 4096;
       const int64_t work = (int64_t)max_kv_len * std::max(B, 1) * std::max(Hkv, 1);
-      chunk = (int)std::max<int64_t>(128, (work + target - 1) / target);
+      chunk = (int)std::max<int64_t>(256, (work + target - 1) / target);
     }
   }
   chunk = (chunk + 15) / 16 * 16;

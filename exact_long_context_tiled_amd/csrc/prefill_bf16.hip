@@ -29,14 +29,26 @@
 namespace attn {
 namespace {
 
-constexpr int kWaves = 8;                  // 2 per SIMD: one wave's softmax overlaps the other's MFMAs
-constexpr int kRowsPerWG = 32 * kWaves;    // 32 packed rows per wave
+constexpr int kWaves = 4;                  // 4 waves x 32 packed rows; two work-groups per CU
+constexpr int kRowsPerWG = 32 * kWaves;
 constexpr int kBK = 64;                    // keys per tile
 constexpr int kThreads = 64 * kWaves;
+constexpr int kXcds = 8;                   // MI355X dispatches work-groups round-robin over 8 XCDs
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
 typedef __attribute__((__vector_size__(8 * sizeof(short)))) short i16x8;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Asynchronous 16-byte copy from global memory to LDS (lane i writes LDS
+// offset 16*i from the wave-uniform destination).  The builtin only exists in
+// the device compilation pass; the host pass only needs the declaration.
+__device__ __forceinline__ void copy16_to_lds(const void* src, lds_void* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+#endif
+}
 
 __device__ __forceinline__ int perm_row(int m) {
   // swap bits 2 and 3
@@ -57,33 +69,63 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// LDS tiles hold kBK rows of D bf16 without padding; the 16-byte chunks of a
+// row are XOR-swizzled so that the matrix-core operand reads are free of
+// bank conflicts:
+//   K: chunk c of row r sits at c ^ (r mod chunks-per-row)
+//      (16 lanes read 16 rows, one chunk each)
+//   V: chunk c of row r sits at c ^ (D/32)*(r & 3)
+//      (transposed reads: 4 rows x 2 chunks per 16-lane group, two groups
+//      2 chunks apart)
+// A tile is filled by direct global->LDS copies: lane i of a copy writes the
+// 16 bytes at LDS offset 16*i, so it fetches the global chunk that belongs
+// there.
 template <int D>
 struct Tile {
-  static constexpr int KP = D + 8;   // K row pitch (bf16): consecutive rows shift by 4 banks
-  static constexpr int VP = D + 32;  // V row pitch: transposed reads of 4 rows hit disjoint banks
-  static constexpr int K_ELEMS = kBK * KP;
-  static constexpr int V_ELEMS = kBK * VP;
-  static constexpr int BUF = K_ELEMS + V_ELEMS;
-  static constexpr int BYTES = 2 * BUF * 2;  // double buffered
-  static constexpr int CPR = D / 8;          // 16-byte chunks per row
-  static constexpr int NCH = kBK * CPR / kThreads;  // chunks of K (and of V) per thread
+  static constexpr int ROWB = D * 2;                // bytes per row
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int BYTES = kBK * ROWB;          // one K (or V) tile
+  static constexpr int STAGE = 2 * BYTES;           // K + V
+  static constexpr int LDS = 2 * STAGE;             // two stages
+  static constexpr int ROWS_PER_COPY = 64 / CPR;    // rows one wave-wide copy covers
+  static constexpr int COPIES = kBK / ROWS_PER_COPY / kWaves;  // copies per wave per tile (K or V)
 };
 
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a, int n_row_tiles) {
+__device__ __forceinline__ int swz_k(int r) {
+  return r & (D / 8 - 1);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  return (D / 32) * (r & 3);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(PrefillArgs a, int n_row_tiles) {
   using TL = Tile<D>;
   constexpr int NKK = D / 16;  // 16-wide chunks of D for S = Q K^T
   constexpr int NDB = D / 32;  // 32-row blocks of D for O^T
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int tile = n_row_tiles - 1 - (int)blockIdx.x;  // heaviest (causal) tiles first
-  const int hk = blockIdx.y;
-  const int b = blockIdx.z;
+
+  // XCD-aware work mapping: work-group L runs on XCD L % 8; give each XCD a
+  // contiguous range of (sequence, KV head, row tile) items so the K/V of one
+  // (sequence, KV head) is reused from that XCD's L2.  Within a pair, the
+  // row tiles that see the most keys go first.
+  const int total = n_row_tiles * a.Hkv * a.B;
+  const int L = blockIdx.x;
+  const int xcd = L % kXcds, kidx = L / kXcds;
+  const int per = total / kXcds, rem = total % kXcds;
+  const int W = xcd * per + min(xcd, rem) + kidx;
+  const int pair = W / n_row_tiles;
+  const int tile = n_row_tiles - 1 - (W - pair * n_row_tiles);
+  const int hk = pair % a.Hkv;
+  const int b = pair / a.Hkv;
   const int G = a.G;
 
   const int64_t rows_total = a.n_q * G;
@@ -120,116 +162,113 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillArgs a
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-  float m = -INFINITY;  // running max of the scaled scores (log2 domain)
+  float m = -INFINITY;  // reference max of the scaled scores (log2 domain)
   float l = 0.f;        // this lane's half of the running sum
 
+  // ---- direct global -> LDS copies of one K/V tile
   const uint16_t* kbase = (const uint16_t*)a.k + b * a.k_sb + (int64_t)hk * D;
   const uint16_t* vbase = (const uint16_t*)a.v + b * a.k_sb + (int64_t)hk * D;
-  const int64_t nk1 = a.n_k - 1;
-
-  // global -> registers for one K/V tile; keys past the block are clamped (and zeroed when stored)
-  uint4 kpre[TL::NCH], vpre[TL::NCH];
-  auto load_tile = [&](int t) {
+  const int nk1 = (int)(a.n_k - 1);  // the host keeps n_k < 2^31 per launch
+  const int cp_row = lane / TL::CPR;  // row within a copy
+  const int cp_chunk = lane % TL::CPR;
+  auto issue_tile = [&](int t, int stage) {
+    char* kst = lds + stage * TL::STAGE;
+    char* vst = kst + TL::BYTES;
 #pragma unroll
-    for (int i = 0; i < TL::NCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int key = c / TL::CPR;
-      const int col = (c % TL::CPR) * 8;
-      const int64_t j = min((int64_t)t * kBK + key, nk1);
-      kpre[i] = *(const uint4*)(kbase + j * a.k_ss + col);
-      vpre[i] = *(const uint4*)(vbase + j * a.k_ss + col);
-    }
-  };
-  auto store_tile = [&](int t, int buf) {
-    uint16_t* Ks = lds + buf * TL::BUF;
-    uint16_t* Vs = Ks + TL::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < TL::NCH; ++i) {
-      const int c = tid + kThreads * i;
-      const int key = c / TL::CPR;
-      const int col = (c % TL::CPR) * 8;
-      const bool in = (int64_t)t * kBK + key <= nk1;
-      *(uint4*)(Ks + key * TL::KP + col) = in ? kpre[i] : uint4{0, 0, 0, 0};
-      *(uint4*)(Vs + key * TL::VP + col) = in ? vpre[i] : uint4{0, 0, 0, 0};
+    for (int c = 0; c < TL::COPIES; ++c) {
+      const int q = w * TL::COPIES + c;  // copy index within the tile
+      const int rr = q * TL::ROWS_PER_COPY + cp_row;
+      const int j = min(t * kBK + rr, nk1);  // keys past the block: finite copies, masked below
+      const int64_t row_off = (int64_t)j * a.k_ss;
+      copy16_to_lds(kbase + row_off + 8 * (cp_chunk ^ swz_k<D>(rr)), (lds_void*)(kst + q * 1024));
+      copy16_to_lds(vbase + row_off + 8 * (cp_chunk ^ swz_v<D>(rr)), (lds_void*)(vst + q * 1024));
     }
   };
 
-  // per-lane LDS offsets of the matrix-core operands
-  const int krow = perm_row(n);
+  // V^T by transposed reads: lane (a=r16/4, b=r16%4) of each 16-lane group
+  // addresses key row 8*(lane/32) + a (+4), columns 16*(g16%2) + 4*b
   const int g16 = lane >> 4, r16 = lane & 15;
-  // V^T operand by transposed reads: lane (a=r16/4, b=r16%4) of each 16-lane group
-  // addresses key row 8*(g16/2) + a (+4), columns 16*(g16%2) + 4*b
-  const int v_off = (8 * (g16 >> 1) + (r16 >> 2)) * TL::VP + 16 * (g16 & 1) + 4 * (r16 & 3);
+  const int v_row = 8 * (g16 >> 1) + (r16 >> 2);       // + 16*c (+4)
+  const int v_col = 16 * (g16 & 1) + 4 * (r16 & 3);    // + 32*db (elements)
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0, 0);
-  }
-  __syncthreads();
+  if (ntiles > 0) issue_tile(0, 0);
   for (int t = 0; t < ntiles; ++t) {
     const int cur = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    const uint16_t* Ks = lds + cur * TL::BUF;
-    const uint16_t* Vs = Ks + TL::K_ELEMS;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t have landed
+    __syncthreads();                     // ... everyone's; and tile t-1 is fully consumed
+    if (t + 1 < ntiles) issue_tile(t + 1, cur ^ 1);
+    const char* Ks = lds + cur * TL::STAGE;
+    const char* Vs = Ks + TL::BYTES;
     const int64_t k0 = (int64_t)t * kBK;
 
     f32x16 s[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       s[mb] = f32x16{};
-      const uint16_t* kr = Ks + (32 * mb + krow) * TL::KP + 8 * hh;
+      const int kr = 32 * mb + perm_row(n);
+      const char* rowp = Ks + kr * TL::ROWB;
+      const int sw = swz_k<D>(kr);
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) s[mb] = mfma32(*(const bf16x8*)(kr + 16 * kk), qf[kk], s[mb]);
+      for (int kk = 0; kk < NKK; ++kk)
+        s[mb] = mfma32(*(const lds_bf16x8*)(rowp + 16 * ((2 * kk + hh) ^ sw)), qf[kk], s[mb]);
     }
     if (k0 + kBK > kfull) {  // tile reaches past the keys every row sees: mask per element
+      const int rel = (int)max(min(lim - k0, (int64_t)kBK), (int64_t)-1);  // last visible key in the tile
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t key = k0 + 32 * mb + 16 * (i >> 3) + 8 * hh + (i & 7);
-          if (key > lim) s[mb][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (32 * mb + 16 * (i >> 3) + 8 * hh + (i & 7) > rel) s[mb][i] = -INFINITY;
     }
-    float tmax = fmaxf(s[0][0], s[0][1]);
+    float tmax = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) tmax = fmaxf(tmax, fmaxf(s[0][i], s[0][i + 1]));
+    for (int i = 3; i < 15; i += 2) tmax = fmaxf(fmaxf(tmax, s[0][i]), s[0][i + 1]);
+    tmax = fmaxf(fmaxf(tmax, s[0][15]), s[1][0]);
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) tmax = fmaxf(tmax, fmaxf(s[1][i], s[1][i + 1]));
+    for (int i = 1; i < 15; i += 2) tmax = fmaxf(fmaxf(tmax, s[1][i]), s[1][i + 1]);
+    tmax = fmaxf(tmax, s[1][15]);
     tmax = half_swap_max(tmax);
-    // scale > 0, so the max of the raw scores times scale*log2(e) is the scaled max
-    const float m_new = fmaxf(m, tmax * a.scale_log2);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-    m = m_new;
-    float psum = 0.f;
+    // scale > 0, so the max of the raw scores times scale*log2(e) is the scaled max.
+    // The reference max m only moves when a tile exceeds it by more than 8
+    // (log2 units): p then stays <= 256 and the rescale of the accumulators is
+    // skipped for the whole wave on most tiles.  Any reference gives the
+    // exact result; the final lse uses the one actually applied.
+    const float tx = tmax * a.scale_log2;
+    if (__builtin_amdgcn_ballot_w64(tx > m + 8.f) != 0) {
+      const float m_new = fmaxf(m, tx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    }
+    const float m_use = m == -INFINITY ? 0.f : m;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
     bf16x8 pf[4];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][i], a.scale_log2, -m_use));
-        psum += p;
+        ps[i & 3] += p;
         pf[2 * mb + (i >> 3)][i & 7] = (__bf16)p;
       }
     }
-    l = l * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint16_t* vp = Vs + v_off + 16 * c * TL::VP + 32 * db;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vp);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 4 * TL::VP));
+        const int row = 16 * c + v_row;
+        const int col = 32 * db + v_col;
+        const char* p0 = Vs + row * TL::ROWB + 16 * ((col >> 3) ^ swz_v<D>(row)) + 2 * (col & 7);
+        const char* p1 = Vs + (row + 4) * TL::ROWB + 16 * ((col >> 3) ^ swz_v<D>(row + 4)) + 2 * (col & 7);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
         const i16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, v8);
-        acc[db] = mfma32(vf, pf[c], acc[db]);
+        acc[db] = mfma32(__builtin_bit_cast(bf16x8, v8), pf[c], acc[db]);
       }
     }
-    if (t + 1 < ntiles) store_tile(t + 1, cur ^ 1);
-    __syncthreads();
   }
 
   const float lt = half_swap_sum(l);
@@ -284,12 +323,13 @@ attn_status launch_d(const PrefillArgs& a, int tiles, hipStream_t stream) {
   (void)hipGetDevice(&dev);
   if (dev >= 0 && dev < 64 && !attr_set[dev]) {
     const hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, Tile<D>::BYTES);
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, Tile<D>::LDS);
     if (e != hipSuccess) return set_error(ATTN_E_DEVICE, "prefill_bf16: LDS attribute: %s", hipGetErrorString(e));
     attr_set[dev] = true;
   }
-  dim3 grid((unsigned)tiles, a.Hkv, a.B);
-  hipLaunchKernelGGL(prefill_bf16_kernel<D>, grid, dim3(kThreads), Tile<D>::BYTES, stream, a, tiles);
+  const int64_t total = (int64_t)tiles * a.Hkv * a.B;
+  if (total > 0x7fffffff) return set_error(ATTN_E_UNSUPPORTED, "prefill: too many work-groups per launch");
+  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)total), dim3(kThreads), Tile<D>::LDS, stream, a, tiles);
   return check_launch("prefill_bf16");
 }
 
@@ -300,6 +340,7 @@ attn_status launch_prefill_bf16(const PrefillArgs& a, int D, hipStream_t stream)
   const int64_t tiles = (rows + kRowsPerWG - 1) / kRowsPerWG;
   if (tiles == 0 || a.B == 0) return ATTN_OK;
   if (tiles > 0x7fffffff) return set_error(ATTN_E_UNSUPPORTED, "prefill: too many query rows per launch");
+  if (a.n_k > 0x7fffff00) return set_error(ATTN_E_UNSUPPORTED, "prefill: more than 2^31 - 256 keys per launch");
   return D == 128 ? launch_d<128>(a, (int)tiles, stream) : launch_d<64>(a, (int)tiles, stream);
 }
 

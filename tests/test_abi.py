@@ -165,3 +165,17 @@ def test_stream_budget_errors():
     with pytest.raises(AttnError) as e:
         attn.stream_plan("bf16", 1, 32, 8, 4096, 4096, 96, budget=1 << 30)
     assert e.value.status == 2
+
+
+def test_library_has_no_undefined_internal_symbols():
+    """Every kernel the library launches is defined in it (a kernel whose host
+    stub is silently not emitted shows up as an undefined attn:: symbol)."""
+    import shutil
+    import subprocess
+
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-C", "--undefined-only", attn.lib_path()], capture_output=True, text=True).stdout
+    bad = [l for l in out.splitlines() if "attn::" in l]
+    assert not bad, bad

@@ -298,7 +298,7 @@ def test_stream_budgeted_small(kind):
         else:
             check_lp(o, lse, ro, rl, f"stream bf16 {bq}x{bk}")
         # f32: merge order only; bf16: P is rounded to bf16 against each key block's own max
-        tol = 1e-5 if kind == "f32" else 2e-3
+        tol = 1e-5 if kind == "f32" else 5e-3
         assert max_abs_err(o, o_dev) <= tol and lse_err(lse, l_dev) <= 1e-4
         outs.append(o)
     o_again, _, _ = attn.stream_budgeted(qh, kh, vh, causal=True, scale=case["scale"], budget=64 << 20,

@@ -246,7 +246,8 @@ def test_decode_equals_last_prefill_row():
              "Hkv": 2, "D": 128, "lengths": np.array([T, T], np.int32), "kv": "bf16", "page_table": None,
              "page_size": T, "paged": False, "scale": case["scale"]}
     od, ld = gpu_decode(dcase)
-    assert max_abs_err(od, o[:, -1]) <= 5e-3 and lse_err(ld, lse[:, :, -1]) <= 1e-4
+    # decode sums fp32 weights; prefill sums the bf16-rounded weights its P.V product uses
+    assert max_abs_err(od, o[:, -1]) <= 5e-3 and lse_err(ld, lse[:, :, -1]) <= 1e-3
 
 
 # ------------------------------------------------------------------ merge
@@ -299,7 +300,7 @@ def test_stream_budgeted_small(kind):
             check_lp(o, lse, ro, rl, f"stream bf16 {bq}x{bk}")
         # f32: merge order only; bf16: P is rounded to bf16 against each key block's own max
         tol = 1e-5 if kind == "f32" else 5e-3
-        assert max_abs_err(o, o_dev) <= tol and lse_err(lse, l_dev) <= 1e-4
+        assert max_abs_err(o, o_dev) <= tol and lse_err(lse, l_dev) <= (1e-4 if kind == "f32" else 1e-3)
         outs.append(o)
     o_again, _, _ = attn.stream_budgeted(qh, kh, vh, causal=True, scale=case["scale"], budget=64 << 20,
                                          block_q=256, block_k=128)

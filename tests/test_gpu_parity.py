@@ -325,3 +325,56 @@ def test_stream_budget_too_small_fails_before_allocating():
         attn.stream_budgeted(qh, kh, vh, causal=True, budget=4096)
     assert e.value.status == 3
     assert torch.cuda.mem_get_info()[0] == free0
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_stream_cqsa_million_token_causal():
+    """B=1 Hq=32 Hkv=8 S=T=2^20 D=128 bf16 causal from pinned host memory under a 4 GB
+    device budget: checked against the unbudgeted on-device run on every output and
+    against the fp64 oracle on 64 seeded query rows x all heads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    w = gen.WORKLOADS["stream_cqsa_causal_1m"]
+    B, Hq, Hkv, S, T, D = w["B"], w["Hq"], w["Hkv"], w["S"], w["T"], w["D"]
+    seed = 0x5EED + 5
+    hq = torch.empty((B, S, Hq, D), dtype=torch.int16, pin_memory=True)
+    hk = torch.empty((B, T, Hkv, D), dtype=torch.int16, pin_memory=True)
+    hv = torch.empty((B, T, Hkv, D), dtype=torch.int16, pin_memory=True)
+    qn = gen.normal(hq.shape, seed, gen.TID_Q, "bf16", out=hq.numpy().view(np.uint16))
+    kn = gen.normal(hk.shape, seed, gen.TID_K, "bf16", out=hk.numpy().view(np.uint16))
+    vn = gen.normal(hv.shape, seed, gen.TID_V, "bf16", out=hv.numpy().view(np.uint16))
+    say("stream 1M: inputs generated")
+    rows = gen.sample_rows(S, 64, seed)
+    scale = 1.0 / math.sqrt(D)
+    with ThreadPoolExecutor(max_workers=1) as ex:
+        fut = ex.submit(oracle.attention, qn, kn, vn, B=B, Hq=Hq, Hkv=Hkv, S=S, T=T, D=D, causal=True,
+                        scale=scale, rows=rows)
+        o_h, lse_h, rep = attn.stream_budgeted(hq.view(torch.bfloat16), hk.view(torch.bfloat16),
+                                               hv.view(torch.bfloat16), causal=True, scale=scale,
+                                               budget=w["budget"])
+        say(f"stream 1M: {rep}")
+        assert rep["peak_device_bytes"] <= w["budget"]
+        assert rep["d2h_bytes"] == S * Hq * D * 4 + S * Hq * 4
+        # the unbudgeted run, all on the device
+        od, ld = attn.prefill(hq.view(torch.bfloat16).cuda(), hk.view(torch.bfloat16).cuda(),
+                              hv.view(torch.bfloat16).cuda(), causal=True, scale=scale)
+        torch.cuda.synchronize()
+        say("stream 1M: device run done")
+        worst_o = worst_l = 0.0
+        step = 1 << 16
+        for s0 in range(0, S, step):
+            a_ = o_h[:, s0:s0 + step].cuda()
+            worst_o = max(worst_o, float((a_ - od[:, s0:s0 + step]).abs().max()))
+        ld_h = lse_h.cuda()
+        worst_l = float((ld_h - ld).abs().max())
+        del od
+        say(f"stream 1M vs device: max_abs={worst_o:.3e} lse={worst_l:.3e}")
+        assert worst_o <= 5e-3 and worst_l <= 1e-3
+        assert bool(torch.isfinite(ld_h).all())
+        ro, rl = fut.result()
+    o_s = o_h.numpy()[:, rows]
+    l_s = lse_h.numpy()[:, :, rows]
+    check_lp(o_s, l_s, ro, rl, "stream 1M sampled rows")

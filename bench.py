@@ -33,10 +33,42 @@ if ROOT not in sys.path:
 METRIC = "attention TFLOP/s (prefill) + decode KV GB/s, as fraction of MI355X peak"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk (dense, published 2.5 PF)
 PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "exact_long_context_tiled_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(*names):
+    """sha256 of the kernel sources a measurement belongs to."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(profile, *sources):
+    """HBM bytes per launch recorded from PMC counters in a committed profile,
+    or None if the profile is missing or the kernel source changed since."""
+    path = os.path.join(PROFILES, profile)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != source_digest(*sources):
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def causal_pairs(S, T):
@@ -135,7 +167,8 @@ def bench_decode(args):
             round(ms * 1e3, 3), "bytes": nbytes, "valid_tokens": valid_tokens, "lengths": lens.tolist(),
             "cache_copies": copies, "steps": steps,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": recorded_traffic("decode_paged_bf16_pmc_traffic.md", "decode.hip", "merge.hip")}}
 
 
 def cpu_baseline(case, w, target_s):
@@ -198,6 +231,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--stream", action="store_true", help="also run the 2^20-token budgeted streaming workload")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device-to-device copy three times (PMC byte-counter reference)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (sharding is a design note only); "
@@ -225,12 +260,20 @@ def main():
         "config": {"workload": "llama13b_gqa_causal_bf16", "B": w["B"], "Hq": w["Hq"], "Hkv": w["Hkv"],
                    "S": w["S"], "T": w["T"], "D": w["D"], "causal": True, "flop_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": recorded_traffic("prefill_llama13b_pmc_traffic.md", "prefill_bf16.hip")},
     }
     if not args.no_decode:
         out["decode"] = bench_decode(args)
     if args.stream:
         out["stream"] = bench_stream(args)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = src.numel() * 4
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(case, w, args.cpu_seconds)
     print(json.dumps(out), flush=True)

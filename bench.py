@@ -168,7 +168,7 @@ def bench_decode(args):
             "cache_copies": copies, "steps": steps,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": recorded_traffic("decode_paged_bf16_pmc_traffic.md", "decode.hip", "merge.hip")}}
+                         "traffic": recorded_traffic("decode_paged_bf16_pmc_traffic.md", "decode.hip")}}
 
 
 def cpu_baseline(case, w, target_s):

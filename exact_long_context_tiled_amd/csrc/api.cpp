@@ -91,8 +91,8 @@ extern "C" attn_status attn_prefill(attn_dtype dt, const void* q, const void* k,
 }
 
 extern "C" size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len, int num_splits) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_kv_len < 0 || num_splits < 0) return 0;
-  return decode_workspace_bytes(B, Hq, D, plan_decode(B, Hq, Hkv, max_kv_len, num_splits));
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_kv_len < 0 || num_splits < 0 || Hq % Hkv) return 0;
+  return decode_workspace_bytes(B, Hkv, Hq / Hkv, D, num_splits > 0 ? num_splits : kDecodeMaxAutoUnits);
 }
 
 extern "C" attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, const void* k_cache,
@@ -110,6 +110,9 @@ extern "C" attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, cons
   const int G = Hq / Hkv;
   if (G > 8) return set_error(ATTN_E_UNSUPPORTED, "decode: at most 8 query heads per KV head (got %d)", G);
   if (!isfinite(scale)) return set_error(ATTN_E_INVALID, "decode: scale must be finite");
+  if (num_splits > kDecodeMaxUnits)
+    return set_error(ATTN_E_UNSUPPORTED, "decode: at most %d work units (got %d)", kDecodeMaxUnits, num_splits);
+  if (B > 4095) return set_error(ATTN_E_UNSUPPORTED, "decode: at most 4095 sequences per call (got %d)", B);
   if (B == 0) return ATTN_OK;
   if (!q || !k_cache || !v_cache || !kv_lens || !o) return set_error(ATTN_E_INVALID, "decode: null device pointer");
   if (kv_dt != ATTN_BF16 && (!k_scale || !v_scale))
@@ -127,13 +130,14 @@ extern "C" attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, cons
     if (page_size < max_kv_len)
       return set_error(ATTN_E_INVALID, "decode: contiguous cache needs page_size >= max_kv_len");
   }
-  const DecodePlan plan = plan_decode(B, Hq, Hkv, max_kv_len, num_splits);
-  const size_t need = decode_workspace_bytes(B, Hq, D, plan);
+  // group positions times unit counts must stay inside int64
+  const double groups = (double)B * Hkv * ((max_kv_len + kDecodeGroup - 1) / kDecodeGroup);
+  if (groups * (num_splits > 0 ? num_splits : kDecodeMaxAutoUnits) > 4e18)
+    return set_error(ATTN_E_UNSUPPORTED, "decode: batch too large");
+  const size_t need = decode_workspace_bytes(B, Hkv, G, D, num_splits > 0 ? num_splits : kDecodeMaxAutoUnits);
   if (!workspace || workspace_bytes < need)
     return set_error(ATTN_E_INVALID, "decode: workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
   if (((uintptr_t)workspace) & 255) return set_error(ATTN_E_INVALID, "decode: workspace must be 256-byte aligned");
-  if (plan.n_splits > 65535 || Hkv > 65535 || B > 65535)
-    return set_error(ATTN_E_UNSUPPORTED, "decode: grid too large");
   DecodeArgs a{};
   a.q = q;
   a.k = k_cache;
@@ -145,19 +149,21 @@ extern "C" attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, cons
   a.page_size = page_size;
   a.page_shift = shift;
   a.kv_lens = kv_lens;
+  a.max_kv_len = max_kv_len;
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
-  a.chunk = plan.chunk;
-  a.n_splits = plan.n_splits;
+  a.n_units = num_splits;
   a.scale_log2 = scale * kLog2e;
-  const size_t rows = (size_t)plan.n_splits * (size_t)B * (size_t)Hq;
-  a.part_o = (float*)workspace;
-  a.part_lse = (float*)((char*)workspace + (rows * (size_t)D * sizeof(float) + 255) / 256 * 256);
-  hipStream_t s = (hipStream_t)stream;
-  attn_status st = launch_decode_split(kv_dt, a, D, G, s);
-  if (st != ATTN_OK) return st;
-  return launch_merge(plan.n_splits, a.part_o, a.part_lse, (int64_t)B * Hq, D, o, lse, s);
+  const size_t segs = (size_t)B * Hkv;
+  const size_t rec_bytes =
+      ((size_t)((num_splits > 0 ? num_splits : kDecodeMaxAutoUnits) + segs) * decode_record_floats(G, D) *
+           sizeof(float) + 255) / 256 * 256;
+  a.part = (float*)workspace;
+  a.seg_info = (int32_t*)((char*)workspace + rec_bytes);
+  a.o = o;
+  a.lse = lse;
+  return launch_decode(kv_dt, a, D, G, (hipStream_t)stream);
 }
 
 extern "C" attn_status attn_merge_partials(int n, const float* o_parts, const float* lse_parts, int64_t R, int D,

@@ -56,6 +56,11 @@ attn_status launch_prefill_bf16(const PrefillArgs& a, int D, hipStream_t stream)
 attn_status launch_prefill_f32(const PrefillArgs& a, int D, hipStream_t stream);
 
 // ---------------------------------------------------------------- decode
+// The KV of the whole batch is one run of 16-token groups, segment by
+// segment ((sequence, KV head) in order, ceil(len / 16) groups each); work
+// unit i of N takes groups [floor(i*W/N), floor((i+1)*W/N)).  A unit yields
+// one partial record per segment it touches (record index i + segment); a
+// segment covered by one unit alone is written straight to the output.
 struct DecodeArgs {
   const void* q;  // [B, Hq, D] bf16
   const void* k;  // cache
@@ -67,22 +72,25 @@ struct DecodeArgs {
   int page_size;
   int page_shift;  // log2(page_size) when paged
   const int32_t* kv_lens;
+  int max_kv_len;  // lengths are clamped to [0, max_kv_len]
   int B, Hq, Hkv;
-  int chunk;     // tokens per split (multiple of 16)
-  int n_splits;  // splits per sequence in the grid
+  int n_units;  // N
   float scale_log2;
-  float* part_o;    // [n_splits, B*Hq, D]
-  float* part_lse;  // [n_splits, B*Hq]
+  float* part;       // records [N + B*Hkv - 1][G*D + 16]: O rows, then lse (log2) padded to 16
+  int32_t* seg_info; // [B*Hkv][2]: first record, record count (written by the segment's first unit)
+  float* o;          // [B, Hq, D]
+  float* lse;        // [B, Hq] or null
 };
 
-struct DecodePlan {
-  int chunk;
-  int n_splits;
-};
-DecodePlan plan_decode(int B, int Hq, int Hkv, int max_kv_len, int num_splits);
-size_t decode_workspace_bytes(int B, int Hq, int D, const DecodePlan& p);
+constexpr int kDecodeGroup = 16;          // tokens per group (>= tokens per wave load step)
+constexpr int kDecodeMaxAutoUnits = 2048; // upper bound of the automatic unit count
+constexpr int kDecodeMaxUnits = 65535;
 
-attn_status launch_decode_split(attn_dtype kv_dt, const DecodeArgs& a, int D, int G, hipStream_t stream);
+int decode_record_floats(int G, int D);
+size_t decode_workspace_bytes(int B, int Hkv, int G, int D, int n_units_bound);
+// n_units == 0 picks one work-group per compute unit (at most
+// kDecodeMaxAutoUnits); the merge kernel runs after the split kernel.
+attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a, int D, int G, hipStream_t stream);
 
 // ---------------------------------------------------------------- merge
 attn_status launch_merge(int n, const float* o_parts, const float* lse_parts, int64_t R, int D, float* o,

@@ -1,10 +1,22 @@
 // Split-KV ("flash") decoding: one query token per sequence against a KV
-// cache.  The KV sequence of each (sequence, KV head) is cut into chunks; one
-// work-group per chunk produces, for all G query heads sharing that KV head,
-// the chunk's normalised partial output and its log-sum-exp, and a merge
-// kernel combines the chunks exactly (ONNX Runtime PR #28695 analysis,
-// section 2: parallel KV scan over idle workers + log-sum-exp reduce).
+// cache.  The KV sequence of each (sequence, KV head) is scanned in pieces by
+// independent work-groups; each piece yields, for all G query heads sharing
+// that KV head, a normalised partial output and its log-sum-exp, and the
+// pieces are combined exactly by log-sum-exp (ONNX Runtime PR #28695
+// analysis, section 2: parallel KV scan over idle workers + log-sum-exp
+// reduce).
 //
+// Work split.  The batch's KV is laid end to end as one run of 16-token
+// groups, segment by segment ((sequence, KV head) in order), and cut into N
+// equal runs, one per work-group, N being the number of compute units (one
+// work-group each, all resident at once).  Every work-group streams the same
+// number of bytes whatever the length mix, so all finish together, and the
+// partial results written (one per piece, about N + segments in all, instead
+// of one per fixed-size chunk) stay few: stores mixed into a saturated read
+// stream cost far more than their size.  A segment that one work-group
+// covers whole is written straight to the output; the others are merged by
+// decode_merge_kernel.
+
 // The caches may be paged (fixed-size pages located through a page table:
 // LLM-CoOpt, "Methodology" item 3) and quantised (int8 with a per-token,
 // per-KV-head scale; OCP e4m3fn with a per-KV-head scale: LLM-CoOpt
@@ -14,15 +26,17 @@
 // This is a bandwidth-bound scan, so the vector ALUs do the arithmetic.  The
 // lanes of a wave form token slots of D*bytes/16 lanes, each lane owning one
 // 16-byte slice of a token's K and V rows; every iteration a wave loads the K
-// and V slices of 4 tokens per slot (all loads in flight together), reduces
+// and V slices of U tokens per slot (all loads in flight together), reduces
 // the slice dot products across the slot with row-local DPP moves, and
 // folds the tokens into a per-slot online softmax (running max, sum and
 // output accumulator).  bf16 K is dotted with the exact bf16 query in packed
-// bf16 pairs; int8 / fp8 slices are converted to fp32.  At the end the slots
-// of a wave, then the four waves, are combined by the same max/rescale rule.
-// Pages hold >= 16 tokens, so the page-table entry of each load step is one
-// wave-uniform (scalar) read.
+// bf16 pairs; int8 / fp8 slices are converted to fp32.  At the end of a piece
+// the slots of a wave, then the waves of the work-group, are combined by the same
+// max/rescale rule.  Pieces start on 16-token group boundaries and pages hold
+// a power-of-two number >= 16 of tokens, so the tokens of one wave load step
+// never straddle a page and its page-table entry is one scalar read.
 #include <math.h>
+#include <stdlib.h>
 
 #include <algorithm>
 
@@ -76,15 +90,6 @@ __device__ __forceinline__ void decode16(uint4 raw, float* out) {
   }
 }
 
-// Row index (token row of the cache, without the D dimension).
-__device__ __forceinline__ int64_t cache_row(const DecodeArgs& a, int b, int hk, int t) {
-  if (a.page_table) {
-    const int p = a.page_table[(int64_t)b * a.max_pages + (t >> a.page_shift)];
-    return ((int64_t)p * a.Hkv + hk) * a.page_size + (t & (a.page_size - 1));
-  }
-  return ((int64_t)b * a.Hkv + hk) * a.page_size + t;
-}
-
 // Sum over the LPT lanes (1, 2, 4, 8 or 16 adjacent lanes) that hold one
 // token's slices, with row-local DPP moves (no LDS round trip).
 template <int LPT>
@@ -98,8 +103,87 @@ __device__ __forceinline__ float token_sum(float x) {
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
+// {a, b} = {x of this lane, x of lane ^ OFF} in a lane-fixed order (the
+// combine below is symmetric in the two): one permlane swap for OFF = 32 or
+// 16, a row rotation for OFF = 8, an LDS-free bpermute otherwise.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float x, float& a, float& b) {
+  if constexpr (OFF == 32 || OFF == 16) {
+    const uint32_t u = __float_as_uint(x);
+    const auto r = OFF == 32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                             : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else if constexpr (OFF == 8) {
+    a = x;
+    b = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+  } else {
+    a = x;
+    b = __shfl_xor(x, OFF);
+  }
+}
+
+// Merge the online-softmax states (m, l, acc) of lanes OFF apart.
+template <int OFF, int G, int EPL>
+__device__ __forceinline__ void combine_lanes(float (&m)[G], float (&l)[G], float (&acc)[G][EPL]) {
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float m0, m1, l0, l1;
+    lane_pair<OFF>(m[g], m0, m1);
+    lane_pair<OFF>(l[g], l0, l1);
+    const float M = fmaxf(m0, m1);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    const float f0 = __builtin_amdgcn_exp2f(m0 - Mu), f1 = __builtin_amdgcn_exp2f(m1 - Mu);
+    l[g] = l0 * f0 + l1 * f1;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float a0, a1;
+      lane_pair<OFF>(acc[g][e], a0, a1);
+      acc[g][e] = a0 * f0 + a1 * f1;
+    }
+    m[g] = M;
+  }
+}
+
+__device__ __forceinline__ int clamp_len(int t, int max_len) { return min(max(t, 0), max_len); }
+
+// pre[b] = groups of all segments of sequences < b (per KV head), pre[B] = total;
+// computed by the whole work-group into LDS.
+template <int THREADS>
+__device__ void group_prefix(const int32_t* __restrict__ lens, int B, int max_len, int64_t* pre,
+                             int64_t* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int per = (B + THREADS - 1) / THREADS;
+  const int b0 = tid * per;
+  int64_t s = 0;
+  for (int k = 0; k < per; ++k)
+    if (b0 + k < B) s += (clamp_len(lens[b0 + k], max_len) + kDecodeGroup - 1) / kDecodeGroup;
+  int64_t x = s;  // inclusive scan over the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int64_t base = 0;
+  for (int ww = 0; ww < w; ++ww) base += wsum[ww];
+  int64_t run = base + x - s;
+  for (int k = 0; k < per; ++k) {
+    if (b0 + k < B) {
+      pre[b0 + k] = run;
+      run += (clamp_len(lens[b0 + k], max_len) + kDecodeGroup - 1) / kDecodeGroup;
+    }
+  }
+  if (tid == THREADS - 1) pre[B] = base + x;
+  __syncthreads();
+}
+
+constexpr int kDecodeWaves = 4;  // waves per work-group
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
+
 template <int KV, int D, int G>
-__global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs a) {
   constexpr int EB = KvTraits<KV>::kBytes;
   constexpr int EPL = 16 / EB;   // elements per lane slice
   constexpr int LPT = D / EPL;   // lanes per token
@@ -107,246 +191,402 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeArgs a) {
   constexpr int U = EB == 2 ? 4 : 2;  // load steps per iteration (16 tokens per wave at D = 128)
   constexpr int TPI = TPW * U;   // tokens per wave per iteration
   constexpr bool kDot2 = KV == ATTN_BF16;
-  __shared__ float red_acc[4][G * D];
-  __shared__ float red_m[4][G], red_l[4][G];
+  constexpr int REC = G * D + 16;
+  static_assert(kDecodeGroup % TPW == 0, "a load step must not straddle a group");
+  extern __shared__ int64_t pre[];  // [B + 1]
+  __shared__ float red_acc[kDecodeWaves][G * D];
+  __shared__ float red_m[kDecodeWaves][G], red_l[kDecodeWaves][G];
+  __shared__ int64_t wsum[kDecodeWaves];
 
-  const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int slot = lane / LPT, part = lane % LPT;
-  const int64_t BHq = (int64_t)a.B * a.Hq;
-  const int64_t row0 = (int64_t)b * a.Hq + (int64_t)hk * G;  // first (b, h) row of this group
-  const int T = a.kv_lens[b];
-  const int t0 = split * a.chunk;
-  const int t1 = min(T, t0 + a.chunk);
-  if (t0 >= t1) {  // no token in this chunk: an empty partial
-    if (tid < G) a.part_lse[(int64_t)split * BHq + row0 + tid] = -INFINITY;
-    return;
-  }
-
-  // query slices: exact bf16 pairs for the packed dot (bf16 cache), or fp32
-  // pre-multiplied by scale*log2(e) (and the fp8 per-head K scale)
-  bf16x2 q2[kDot2 ? G : 1][kDot2 ? EPL / 2 : 1];
-  float qf[kDot2 ? 1 : G][kDot2 ? 1 : EPL];
-  float smul = a.scale_log2;
-  {
-    const uint16_t* qb = (const uint16_t*)a.q + row0 * D + part * EPL;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int e = 0; e < EPL; e += 8) {
-        const uint4 raw = *(const uint4*)(qb + (int64_t)g * D + e);
-        if constexpr (kDot2) {
-          const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) q2[g][e / 2 + i] = __builtin_bit_cast(bf16x2, wd[i]);
-        } else {
-          float tmp[8];
-          decode16<ATTN_BF16>(raw, tmp);
-          float qmul = a.scale_log2;
-          if constexpr (KV == ATTN_FP8_E4M3) qmul *= a.k_scale[hk];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) qf[g][e + i] = tmp[i] * qmul;
-        }
-      }
-    }
-    if constexpr (!kDot2) smul = 1.f;
-  }
-
-  float m[G], l[G], acc[G][EPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
-  }
-
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index as a scalar
   const uint8_t* kb = (const uint8_t*)a.k;
   const uint8_t* vb = (const uint8_t*)a.v;
   const int64_t lane_off = (int64_t)part * EPL * EB;
+  constexpr int kStride = kDecodeWaves * TPI;  // tokens between a wave's consecutive iterations
 
-  const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index as a scalar
-  const int64_t hk_rows = (int64_t)hk * a.page_size;
-  constexpr int kStride = 4 * TPI;  // tokens between a wave's consecutive iterations
+  group_prefix<kDecodeThreads>(a.kv_lens, a.B, a.max_kv_len, pre, wsum);
+  const int64_t W = pre[a.B] * a.Hkv;
+  // never more units than groups, so that every unit owns at least one group
+  // and the records of a segment are the consecutive units that cover it
+  const int64_t N = a.n_units < W ? (int64_t)a.n_units : W;
+  const int unit = blockIdx.x;
+  if (unit >= N) return;
+  const int64_t x1 = (unit + 1) * W / N;
 
-  // Loads of one iteration (U steps of TPW tokens).  TPW consecutive tokens
-  // from a TPW-aligned index never straddle a page and every step index is
-  // wave-uniform, so the page-table entries are scalar loads issued first.
-  struct Buf {
-    uint4 kr[U], vr[U];
-    float ksc[U], vsc[U];
-  };
-  // Every call issues the same number of vector loads with no branch around
-  // them (tokens past the chunk are clamped onto its last token, a cache
-  // hit), so the compiler's wait counters keep the next iteration's loads in
-  // flight while the current one is consumed.
-  auto issue = [&](int g0, Buf& bf) {
-    int64_t step_row[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      // wave-uniform and inside the sequence; readfirstlane keeps it (and the
-      // page-table read) on the scalar unit, off the vector-load counter
-      const int tc = __builtin_amdgcn_readfirstlane(min(g0 + u * TPW, t1 - 1));
-      if (a.page_table) {
-        // read through the constant address space: a scalar (SMEM) load
-        const auto* pt = (const __attribute__((address_space(4))) int32_t*)a.page_table;
-        const int pg = pt[(int64_t)b * a.max_pages + (tc >> a.page_shift)];
-        step_row[u] = (int64_t)pg * a.Hkv * a.page_size + hk_rows - (tc & ~(a.page_size - 1));
-      } else {
-        step_row[u] = (int64_t)b * a.Hkv * a.page_size + hk_rows;
-      }
+  for (int64_t pos = unit * W / N; pos < x1;) {
+    // the segment holding group `pos`: the last sequence starting at or before it
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] * a.Hkv <= pos) lo = mid;
+      else hi = mid - 1;
     }
+    const int b = __builtin_amdgcn_readfirstlane(lo);
+    const int64_t sbase = pre[b] * a.Hkv;
+    const int ng = (int)(pre[b + 1] - pre[b]);
+    const int hk = __builtin_amdgcn_readfirstlane((int)((pos - sbase) / ng));
+    const int j0 = (int)(pos - sbase - (int64_t)hk * ng);
+    const int64_t seg_end = sbase + (int64_t)(hk + 1) * ng;
+    const int64_t pend = seg_end < x1 ? seg_end : x1;
+    const int T = clamp_len(a.kv_lens[b], a.max_kv_len);
+    const int t0 = __builtin_amdgcn_readfirstlane(j0 * kDecodeGroup);
+    const int t1 = __builtin_amdgcn_readfirstlane(min(T, (j0 + (int)(pend - pos)) * kDecodeGroup));
+    const int seg = b * a.Hkv + hk;
+    const bool whole = j0 == 0 && pend == seg_end;
+    const int64_t row0 = (int64_t)b * a.Hq + (int64_t)hk * G;  // first (b, h) row of this group
+
+    // query slices: exact bf16 pairs for the packed dot (bf16 cache), or fp32
+    // pre-multiplied by scale*log2(e) (and the fp8 per-head K scale)
+    bf16x2 q2[kDot2 ? G : 1][kDot2 ? EPL / 2 : 1];
+    float qf[kDot2 ? 1 : G][kDot2 ? 1 : EPL];
+    float smul = a.scale_log2;
+    {
+      const uint16_t* qb = (const uint16_t*)a.q + row0 * D + part * EPL;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t row = step_row[u] + min(g0 + u * TPW + slot, t1 - 1);
-      bf.kr[u] = *(const uint4*)(kb + row * (D * EB) + lane_off);
-      bf.vr[u] = *(const uint4*)(vb + row * (D * EB) + lane_off);
-      if constexpr (KV == ATTN_INT8) {
-        bf.ksc[u] = a.k_scale[row];  // q already carries scale*log2(e)
-        bf.vsc[u] = a.v_scale[row];
-      } else {
-        bf.ksc[u] = bf.vsc[u] = 1.f;
-      }
-    }
-  };
-  auto consume = [&](int g0, const Buf& bf) {
-    // scores of the U tokens of this lane's slot, in the log2 domain
-    float s[U][G];
+      for (int g = 0; g < G; ++g) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool ok = g0 + u * TPW + slot < t1;
-      if constexpr (kDot2) {
-        const uint32_t wd[4] = {bf.kr[u].x, bf.kr[u].y, bf.kr[u].z, bf.kr[u].w};
+        for (int e = 0; e < EPL; e += 8) {
+          const uint4 raw = *(const uint4*)(qb + (int64_t)g * D + e);
+          if constexpr (kDot2) {
+            const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float d = 0.f;
+            for (int i = 0; i < 4; ++i) q2[g][e / 2 + i] = __builtin_bit_cast(bf16x2, wd[i]);
+          } else {
+            float tmp[8];
+            decode16<ATTN_BF16>(raw, tmp);
+            float qmul = a.scale_log2;
+            if constexpr (KV == ATTN_FP8_E4M3) qmul *= a.k_scale[hk];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) d = __builtin_amdgcn_fdot2_f32_bf16(q2[g][i], __builtin_bit_cast(bf16x2, wd[i]), d, false);
-          s[u][g] = d;
+            for (int i = 0; i < 8; ++i) qf[g][e + i] = tmp[i] * qmul;
+          }
         }
-      } else {
-        float kv[EPL];
-        decode16<KV>(bf.kr[u], kv);
+      }
+      if constexpr (!kDot2) smul = 1.f;
+    }
+
+    float m[G], l[G], acc[G][EPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
+    }
+    const int64_t hk_rows = (int64_t)hk * a.page_size;
+
+    // Loads of one iteration (U steps of TPW tokens).  TPW consecutive tokens
+    // from a TPW-aligned index never straddle a page and every step index is
+    // wave-uniform, so the page-table entries are scalar loads issued first.
+    struct Buf {
+      uint4 kr[U], vr[U];
+      float ksc[U], vsc[U];
+    };
+    // Every call issues the same number of vector loads with no branch around
+    // them (tokens past the piece are clamped onto its last token, a cache
+    // hit), so the compiler's wait counters keep the next iteration's loads in
+    // flight while the current one is consumed.
+    auto issue = [&](int g0, Buf& bf) {
+      int64_t step_row[U];  // cache row of token 0 of the step's page
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        // first token of the step, wave-uniform and inside the piece;
+        // readfirstlane keeps it (and the page-table read) on the scalar unit
+        const int tc = __builtin_amdgcn_readfirstlane(min(g0 + u * TPW, t1 - 1));
+        if (a.page_table) {
+          // read through the constant address space: a scalar (SMEM) load
+          const auto* pt = (const __attribute__((address_space(4))) int32_t*)a.page_table;
+          const int pg = pt[(int64_t)b * a.max_pages + (tc >> a.page_shift)];
+          step_row[u] = (int64_t)pg * a.Hkv * a.page_size + hk_rows - (tc & ~(a.page_size - 1));
+        } else {
+          step_row[u] = (int64_t)b * a.Hkv * a.page_size + hk_rows;
+        }
+      }
+      // (all scalar work first, then the vector loads back to back; with the
+      // lane's token clamped as a whole index the compiler's wait counters
+      // keep the other buffer's loads in flight)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t row = step_row[u] + min(g0 + u * TPW + slot, t1 - 1);
+        bf.kr[u] = *(const uint4*)(kb + row * (D * EB) + lane_off);
+        bf.vr[u] = *(const uint4*)(vb + row * (D * EB) + lane_off);
+        if constexpr (KV == ATTN_INT8) {
+          bf.ksc[u] = a.k_scale[row];  // q already carries scale*log2(e)
+          bf.vsc[u] = a.v_scale[row];
+        } else {
+          bf.ksc[u] = bf.vsc[u] = 1.f;
+        }
+      }
+    };
+    auto consume = [&](int g0, const Buf& bf) {
+      // raw scores of the U tokens of this lane's slot (int8: times the token's K scale)
+      float s[U][G];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if constexpr (kDot2) {
+          const uint32_t wd[4] = {bf.kr[u].x, bf.kr[u].y, bf.kr[u].z, bf.kr[u].w};
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float d = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              d = __builtin_amdgcn_fdot2_f32_bf16(q2[g][i], __builtin_bit_cast(bf16x2, wd[i]), d, false);
+            s[u][g] = d;
+          }
+        } else {
+          float kv[EPL];
+          decode16<KV>(bf.kr[u], kv);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) d = fmaf(qf[g][e], kv[e], d);
+            s[u][g] = d;
+          }
+        }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          float d = 0.f;
+          s[u][g] = token_sum<LPT>(s[u][g]);
+          if constexpr (KV == ATTN_INT8) s[u][g] *= bf.ksc[u];
+        }
+      }
+      if (g0 + TPI > t1) {  // the piece's last iteration: tokens past its end weigh nothing
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) d = fmaf(qf[g][e], kv[e], d);
-          s[u][g] = d;
+        for (int u = 0; u < U; ++u) {
+          const bool ok = g0 + u * TPW + slot < t1;
+#pragma unroll
+          for (int g = 0; g < G; ++g) s[u][g] = ok ? s[u][g] : -INFINITY;
+        }
+      }
+      float vv[U][EPL];
+#pragma unroll
+      for (int u = 0; u < U; ++u) decode16<KV>(bf.vr[u], vv[u]);
+      // Scores enter the softmax as s*smul (log2 domain, smul > 0).  The
+      // reference max m of a slot only moves when a score exceeds it by more
+      // than 8, so p <= 256 and the rescale of the accumulators is skipped
+      // for the whole wave on most iterations; any reference gives the exact
+      // result.
+      float tx[G];
+      bool grow = false;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float mx = s[0][g];
+#pragma unroll
+        for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][g]);
+        tx[g] = mx * smul;
+        grow |= tx[g] > m[g] + 8.f;
+      }
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const float m_new = fmaxf(m[g], tx[g]);
+          const float alpha = __builtin_amdgcn_exp2f(m[g] - (m_new == -INFINITY ? 0.f : m_new));
+          m[g] = m_new;
+          l[g] *= alpha;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[g][e] *= alpha;
         }
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const float x = token_sum<LPT>(s[u][g]) * (KV == ATTN_INT8 ? bf.ksc[u] : smul);
-        s[u][g] = ok ? x : -INFINITY;
+        const float nm = m[g] == -INFINITY ? 0.f : -m[g];
+        float p[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          p[u] = __builtin_amdgcn_exp2f(fmaf(s[u][g], smul, nm));
+          l[g] += p[u];
+          if constexpr (KV == ATTN_INT8) p[u] *= bf.vsc[u];
+        }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          float x = acc[g][e];
+#pragma unroll
+          for (int u = 0; u < U; ++u) x = fmaf(p[u], vv[u][e], x);
+          acc[g][e] = x;
+        }
       }
-    }
-    // online softmax over the slot's tokens, then accumulate P.V
-    float vv[U][EPL];
-#pragma unroll
-    for (int u = 0; u < U; ++u) decode16<KV>(bf.vr[u], vv[u]);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = s[0][g];
-#pragma unroll
-      for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][g]);
-      const float m_new = fmaxf(m[g], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m[g] - m_use);
-      m[g] = m_new;
-      float lsum = 0.f;
-      float p[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        p[u] = __builtin_amdgcn_exp2f(s[u][g] - m_use);
-        lsum += p[u];
-        if constexpr (KV == ATTN_INT8) p[u] *= bf.vsc[u];
-      }
-      l[g] = l[g] * alpha + lsum;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        float x = acc[g][e] * alpha;
-#pragma unroll
-        for (int u = 0; u < U; ++u) x = fmaf(p[u], vv[u][e], x);
-        acc[g][e] = x;
-      }
-    }
-  };
+    };
 
-  // two-stage software pipeline: the next iteration's loads are in flight
-  // while the current one is consumed
-  Buf b0, b1;
-  int g0 = t0 + wu * TPI;
-  // (the scheduling barriers keep the compiler from sinking a batch of loads
-  // down to its consumer to save registers, which would serialise them)
-  if (g0 < t1) {
-    issue(g0, b0);
-    while (true) {
-      const int g1 = g0 + kStride;
-      issue(g1, b1);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(g0, b0);
-      if (g1 >= t1) break;
-      const int g2 = g1 + kStride;
-      issue(g2, b0);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(g1, b1);
-      if (g2 >= t1) break;
-      g0 = g2;
+    // two-stage software pipeline: the next iteration's loads are in flight
+    // while the current one is consumed.  Two iterations per trip and a
+    // single loop exit: with an exit after each half, the compiler merges
+    // the exits into one latch, and its (path-insensitive) wait counters
+    // would then drain the in-flight buffer at the top of every trip.
+    // (The scheduling barriers keep the compiler from sinking a batch of
+    // loads down to its consumer to save registers, which would serialise
+    // them.)
+    Buf b0, b1;
+    int g0 = t0 + wu * TPI;
+    const int n_it = g0 < t1 ? (t1 - g0 + kStride - 1) / kStride : 0;  // iterations of this wave
+    if (n_it > 0) {
+      issue(g0, b0);
+      int k = 0;
+      for (; k + 2 <= n_it; k += 2) {
+        issue(g0 + kStride, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(g0, b0);
+        issue(g0 + 2 * kStride, b0);  // past the end on the last trip: clamped re-reads
+        __builtin_amdgcn_sched_barrier(0);
+        consume(g0 + kStride, b1);
+        g0 += 2 * kStride;
+      }
+      if (k < n_it) consume(g0, b0);
     }
-  }
 
-  // combine the token slots of the wave (lanes 16/32 apart hold the same d slice)
+    // combine the token slots of the wave (lanes LPT, 2*LPT, ... apart hold the same d slice)
+    if constexpr (LPT <= 4) combine_lanes<4, G, EPL>(m, l, acc);
+    if constexpr (LPT <= 8) combine_lanes<8, G, EPL>(m, l, acc);
+    if constexpr (LPT <= 16) combine_lanes<16, G, EPL>(m, l, acc);
+    combine_lanes<32, G, EPL>(m, l, acc);
+    // combine the waves through LDS
+    if (slot == 0) {
 #pragma unroll
-  for (int off = LPT; off < 64; off <<= 1) {
+      for (int g = 0; g < G; ++g) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float mo = __shfl_xor(m[g], off);
-      const float lo = __shfl_xor(l[g], off);
-      const float M = fmaxf(m[g], mo);
-      const float Mu = M == -INFINITY ? 0.f : M;
-      const float fs = __builtin_amdgcn_exp2f(m[g] - Mu), fo = __builtin_amdgcn_exp2f(mo - Mu);
-      l[g] = l[g] * fs + lo * fo;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[g][e] = acc[g][e] * fs + __shfl_xor(acc[g][e], off) * fo;
-      m[g] = M;
-    }
-  }
-  // combine the four waves through LDS
-  if (slot == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) red_acc[w][g * D + part * EPL + e] = acc[g][e];
-      if (part == 0) {
-        red_m[w][g] = m[g];
-        red_l[w][g] = l[g];
+        for (int e = 0; e < EPL; ++e) red_acc[w][g * D + part * EPL + e] = acc[g][e];
+        if (part == 0) {
+          red_m[w][g] = m[g];
+          red_l[w][g] = l[g];
+        }
       }
     }
-  }
-  __syncthreads();
-  float vmul = 1.f;
-  if constexpr (KV == ATTN_FP8_E4M3) vmul = a.v_scale[hk];
-  for (int idx = tid; idx < G * D; idx += 256) {
-    const int g = idx / D;
-    const float M = fmaxf(fmaxf(red_m[0][g], red_m[1][g]), fmaxf(red_m[2][g], red_m[3][g]));
-    float num = 0.f, den = 0.f;
+    __syncthreads();
+    float vmul = 1.f;
+    if constexpr (KV == ATTN_FP8_E4M3) vmul = a.v_scale[hk];
+    // a piece always holds a key, so every denominator below is positive
+    float* rec = a.part + (int64_t)(unit + seg) * REC;
+    for (int idx = tid; idx < G * D; idx += kDecodeThreads) {
+      const int g = idx / D;
+      float M = red_m[0][g];
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float f = red_m[ww][g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[ww][g] - M);
-      num = fmaf(f, red_acc[ww][idx], num);
-      den = fmaf(f, red_l[ww][g], den);
+      for (int ww = 1; ww < kDecodeWaves; ++ww) M = fmaxf(M, red_m[ww][g]);
+      float num = 0.f, den = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kDecodeWaves; ++ww) {
+        const float f = red_m[ww][g] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[ww][g] - M);
+        num = fmaf(f, red_acc[ww][idx], num);
+        den = fmaf(f, red_l[ww][g], den);
+      }
+      const float val = num * (vmul / den);
+      if (whole) a.o[row0 * D + idx] = val;  // rows row0 .. row0+G-1 are consecutive
+      else rec[idx] = val;
     }
-    a.part_o[((int64_t)split * BHq + row0 + g) * D + (idx - g * D)] = num * (vmul / den);
-    if (idx - g * D == 0) a.part_lse[(int64_t)split * BHq + row0 + g] = (M + __log2f(den)) * kLn2;
+    if (tid < 16) {  // the piece's lse (log2), padded to a whole 64-byte line
+      float v = 0.f;
+      if (tid < G) {
+        float M = red_m[0][tid];
+#pragma unroll
+        for (int ww = 1; ww < kDecodeWaves; ++ww) M = fmaxf(M, red_m[ww][tid]);
+        float den = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kDecodeWaves; ++ww)
+          den = fmaf(red_m[ww][tid] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[ww][tid] - M), red_l[ww][tid], den);
+        v = M + __log2f(den);
+      }
+      if (!whole) rec[G * D + tid] = v;
+      else if (tid < G && a.lse) a.lse[row0 + tid] = v * kLn2;
+    }
+    if (tid == 0 && j0 == 0) {
+      // records of this segment: units unit .. (the unit holding its last group)
+      const int last = whole ? unit : (int)((seg_end * N - 1) / W);
+      a.seg_info[2 * seg] = unit + seg;
+      a.seg_info[2 * seg + 1] = last - unit + 1;
+    }
+    pos = pend;
+    __syncthreads();  // LDS is reused by the next piece
   }
 }
 
+// One wave per output row (b, h): merges the records of its segment by
+// log-sum-exp, or writes O = 0, lse = -inf for an empty sequence.  Segments
+// finished by a single unit were written by the split kernel already.
+template <int D>
+__global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a, int G) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (int64_t)a.B * a.Hq) return;
+  const int lane = threadIdx.x & 63;
+  const int b = (int)(row / a.Hq), h = (int)(row - (int64_t)b * a.Hq);
+  const int hk = h / G, g = h - hk * G;
+  const int seg = b * a.Hkv + hk;
+  // both loads in flight together; seg_info is only meaningful for a non-empty sequence
+  const int T = clamp_len(a.kv_lens[b], a.max_kv_len);
+  const int first = a.seg_info[2 * seg], n = a.seg_info[2 * seg + 1];
+  float* orow = a.o + row * D;
+  constexpr int CPL = D / 64;  // columns per lane
+  if (T == 0) {
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) orow[lane + 64 * k] = 0.f;
+    if (lane == 0 && a.lse) a.lse[row] = -INFINITY;
+    return;
+  }
+  if (n <= 1) return;
+  const int REC = G * D + 16;
+  const float* rec0 = a.part + (int64_t)first * REC;
+  float mx = -INFINITY, den = 0.f, acc[CPL];
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
+  // eight records at a time, all their loads issued before the first use;
+  // an online log-sum-exp update folds each batch in
+  for (int c0 = 0; c0 < n; c0 += 8) {
+    float lv[8], x[8][CPL];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float* rec = rec0 + (int64_t)min(c0 + r, n - 1) * REC;  // past the end: a valid record, weighted 0
+      lv[r] = rec[G * D + g];
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) x[r][k] = rec[g * D + lane + 64 * k];
+    }
+    float bm = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      if (c0 + r >= n) lv[r] = -INFINITY;
+      bm = fmaxf(bm, lv[r]);
+    }
+    const float M = fmaxf(mx, bm);  // finite: every record holds a key
+    const float f = __builtin_amdgcn_exp2f(mx - M);
+    den *= f;
+#pragma unroll
+    for (int k = 0; k < CPL; ++k) acc[k] *= f;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const float w = __builtin_amdgcn_exp2f(lv[r] - M);
+      den += w;
+#pragma unroll
+      for (int k = 0; k < CPL; ++k) acc[k] = fmaf(w, x[r][k], acc[k]);
+    }
+    mx = M;
+  }
+  const float inv = 1.f / den;
+#pragma unroll
+  for (int k = 0; k < CPL; ++k) orow[lane + 64 * k] = acc[k] * inv;
+  if (lane == 0 && a.lse) a.lse[row] = (mx + __log2f(den)) * kLn2;
+}
+
 template <int KV, int D, int G>
-attn_status launch_one(const DecodeArgs& a, hipStream_t stream) {
-  dim3 grid(a.n_splits, a.Hkv, a.B);
-  hipLaunchKernelGGL((decode_split_kernel<KV, D, G>), grid, dim3(256), 0, stream, a);
-  return check_launch("decode_split");
+attn_status launch_one(DecodeArgs a, hipStream_t stream) {
+  const size_t lds = (size_t)(a.B + 1) * sizeof(int64_t);
+  auto kern = decode_split_kernel<KV, D, G>;
+  static bool lds_set = false;  // the length prefix may take the LDS past the default dynamic limit
+  if (!lds_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)((4095 + 1) * sizeof(int64_t))) != hipSuccess)
+      return set_error(ATTN_E_DEVICE, "decode: cannot raise the LDS limit");
+    lds_set = true;
+  }
+  if (a.n_units <= 0) {
+    // one work-group per compute unit: measured faster than filling every
+    // resident slot (fewer partial records, and the scan stays bandwidth-bound)
+    a.n_units = std::min(kDecodeMaxAutoUnits, device_cu_count());
+    const char* env = getenv("ATTN_DECODE_UNITS");
+    if (env && atoi(env) > 0) a.n_units = std::min(kDecodeMaxAutoUnits, atoi(env));
+  }
+  hipLaunchKernelGGL(kern, dim3(a.n_units), dim3(kDecodeThreads), lds, stream, a);
+  attn_status st = check_launch("decode_split");
+  if (st != ATTN_OK) return st;
+  const int64_t rows = (int64_t)a.B * a.Hq;
+  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a, G);
+  return check_launch("decode_merge");
 }
 
 template <int KV, int D>
@@ -371,37 +611,16 @@ attn_status launch_d(const DecodeArgs& a, int D, int G, hipStream_t stream) {
 
 }  // namespace
 
-DecodePlan plan_decode(int B, int Hq, int Hkv, int max_kv_len, int num_splits) {
-  DecodePlan p;
-  int chunk;
-  if (max_kv_len <= 0) {
-    chunk = 16;
-  } else if (num_splits > 0) {
-    chunk = (max_kv_len + num_splits - 1) / num_splits;
-  } else {
-    const char* env = getenv("ATTN_DECODE_CHUNK");
-    if (env && atoi(env) > 0) {
-      chunk = atoi(env);
-    } else {
-      // enough chunks for ~4096 work-groups (16 per CU), never below 256 tokens each
-      const int64_t target = 4096;
-      const int64_t work = (int64_t)max_kv_len * std::max(B, 1) * std::max(Hkv, 1);
-      chunk = (int)std::max<int64_t>(256, (work + target - 1) / target);
-    }
-  }
-  chunk = (chunk + 15) / 16 * 16;
-  p.chunk = chunk;
-  p.n_splits = max_kv_len <= 0 ? 1 : (max_kv_len + chunk - 1) / chunk;
-  return p;
+int decode_record_floats(int G, int D) { return G * D + 16; }
+
+size_t decode_workspace_bytes(int B, int Hkv, int G, int D, int n_units_bound) {
+  const size_t segs = (size_t)B * (size_t)Hkv;
+  const size_t recs = (size_t)n_units_bound + segs;  // record indices stay below N + segments - 1
+  const size_t rec_bytes = (recs * (size_t)decode_record_floats(G, D) * sizeof(float) + 255) / 256 * 256;
+  return rec_bytes + (segs * 2 * sizeof(int32_t) + 255) / 256 * 256;
 }
 
-size_t decode_workspace_bytes(int B, int Hq, int D, const DecodePlan& p) {
-  const size_t rows = (size_t)p.n_splits * (size_t)B * (size_t)Hq;
-  const size_t o_bytes = (rows * (size_t)D * sizeof(float) + 255) / 256 * 256;
-  return o_bytes + (rows * sizeof(float) + 255) / 256 * 256;
-}
-
-attn_status launch_decode_split(attn_dtype kv_dt, const DecodeArgs& a, int D, int G, hipStream_t stream) {
+attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a, int D, int G, hipStream_t stream) {
   switch (kv_dt) {
     case ATTN_BF16: return launch_d<ATTN_BF16>(a, D, G, stream);
     case ATTN_FP8_E4M3: return launch_d<ATTN_FP8_E4M3>(a, D, G, stream);

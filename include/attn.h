@@ -85,9 +85,10 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len,
 
 /*
  * Split-KV ("flash") decoding of one query token per sequence against a KV
- * cache: the KV sequence of each (sequence, KV head) is cut into chunks, each
- * chunk yields a normalised partial output and its lse, and the partials are
- * merged exactly by log-sum-exp.  (Flash decoding: ONNX Runtime PR #28695
+ * cache: the KV sequences of all (sequence, KV head) pairs, laid end to end
+ * in 16-token groups, are cut into equal runs, one per work unit; each piece
+ * of a sequence yields a normalised partial output and its lse, and the
+ * pieces are merged exactly by log-sum-exp.  (Flash decoding: ONNX Runtime PR #28695
  * analysis, section 2; 512-token pages: LLM-CoOpt "Methodology" item 3;
  * FP8 / INT8 caches dequantised on the fly: LLM-CoOpt "Methodology" item 1,
  * ONNX Runtime PR #28695 analysis, introduction and section 1.)
@@ -107,9 +108,11 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len,
  *               last page are never read.  Paged mode needs page_size a power
  *               of two and a multiple of 16.
  *   kv_lens     device int32 [B]: tokens of each sequence (0..max_kv_len).
- *   max_kv_len  host int: upper bound of kv_lens (sizes the split plan).
- *   num_splits  0 = automatic (enough chunks to fill the GPU), else the
- *               maximum number of chunks per sequence.
+ *   max_kv_len  host int: upper bound of kv_lens (lengths are clamped to
+ *               [0, max_kv_len]).
+ *   num_splits  0 = automatic (one work unit per compute unit, at most
+ *               2048), else the number of work units (<= 65535) the batch's
+ *               KV is divided into.  B <= 4095.
  *   workspace   device, >= attn_decode_workspace_size(...) bytes, 256-byte
  *               aligned; scratch for the partials, owned by the caller, not
  *               read before being written.

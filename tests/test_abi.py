@@ -72,12 +72,21 @@ def test_decode_and_merge_validation():
     assert L.attn_merge_partials(2, None, None, 10, 0, None, None, None) == 2
     assert L.attn_merge_partials(2, None, None, 10, 64, None, None, None) == 1
     assert L.attn_merge_partials(2, None, None, 0, 64, None, None, None) == 0
-    # workspace sizing is pure host arithmetic and monotone in the length
+    assert call(B=4096) == 2  # more sequences than the on-chip length prefix holds
+    assert call(ns=65536) == 2  # more work units than one grid dimension
+    # workspace sizing is pure host arithmetic: one record of G*D outputs plus
+    # a 16-float lse line per (work unit + segment), then two ints per segment
     a = attn.decode_workspace_size(8, 32, 8, 128, 4096)
     b = attn.decode_workspace_size(8, 32, 8, 128, 32768)
     assert 0 < a <= b and a % 256 == 0
-    assert attn.decode_workspace_size(8, 32, 8, 128, 32768, num_splits=4) == 2 * (
-        ((4 * 8 * 32 * 128 * 4 + 255) // 256 * 256 + (4 * 8 * 32 * 4 + 255) // 256 * 256) // 2)
+
+    def rnd(x):
+        return (x + 255) // 256 * 256
+
+    assert attn.decode_workspace_size(8, 32, 8, 128, 32768, num_splits=4) == (
+        rnd((4 + 64) * (4 * 128 + 16) * 4) + rnd(64 * 8))
+    assert attn.decode_workspace_size(3, 10, 2, 64, 100, num_splits=7) == (
+        rnd((7 + 6) * (5 * 64 + 16) * 4) + rnd(6 * 8))
 
 
 def _coverage(tasks, rep, S, T, causal, B):

@@ -217,6 +217,20 @@ def test_decode_ragged_edge_cases(kv, paged, page_size, G, D):
         check_lp(o, lse, ro, rl, f"{kv} paged={paged} ps={page_size} G={G} D={D} splits={ns}")
 
 
+def test_decode_many_sequences_mixed_lengths():
+    """B=300 sequences (more than one length per thread of the on-chip prefix sum), with empty,
+    tiny and long ones mixed, over 1, 7, automatic and more work units than token groups."""
+    import oracle
+    rng = np.random.default_rng(7)
+    lens = rng.choice(np.array([0, 1, 5, 16, 33, 700, 3000], np.int32), size=300)
+    case = gen.decode_inputs(300, 8, 2, 128, lens, kv="bf16", page_size=16, paged=True, spare=3, seed=77)
+    ro, rl = oracle.decode(case)
+    for ns in (1, 7, 0, 20000):
+        o, lse = gpu_decode(case, num_splits=ns)
+        assert np.all(o[lens == 0] == 0) and np.all(np.isneginf(lse[lens == 0]))
+        check_lp(o, lse, ro, rl, f"B=300 mixed lengths units={ns}")
+
+
 def test_decode_fp8_every_finite_code():
     """A cache holding every finite e4m3fn byte: the hardware decode must be OCP e4m3fn."""
     import oracle

@@ -86,7 +86,6 @@ struct Tile {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static constexpr int BYTES = kBK * ROWB;          // one K (or V) tile
   static constexpr int STAGE = 2 * BYTES;           // K + V
-  static constexpr int LDS = 2 * STAGE;             // two stages
   static constexpr int ROWS_PER_COPY = 64 / CPR;    // rows one wave-wide copy covers
   static constexpr int COPIES = kBK / ROWS_PER_COPY / kWaves;  // copies per wave per tile (K or V)
 };
@@ -105,7 +104,12 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(PrefillArgs a
   using TL = Tile<D>;
   constexpr int NKK = D / 16;  // 16-wide chunks of D for S = Q K^T
   constexpr int NDB = D / 32;  // 32-row blocks of D for O^T
-  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  // The two stages of the K/V ring are separate arrays and the tile loop is
+  // unrolled by two, so every access names its stage statically: the
+  // compiler can then tell the next tile's direct-to-LDS copies from the
+  // current tile's reads and does not wait for the copies before each read.
+  __shared__ __attribute__((aligned(1024))) char stage0[TL::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[TL::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -171,8 +175,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(PrefillArgs a
   const int nk1 = (int)(a.n_k - 1);  // the host keeps n_k < 2^31 per launch
   const int cp_row = lane / TL::CPR;  // row within a copy
   const int cp_chunk = lane % TL::CPR;
-  auto issue_tile = [&](int t, int stage) {
-    char* kst = lds + stage * TL::STAGE;
+  auto issue_tile = [&](int t, char* kst) {
     char* vst = kst + TL::BYTES;
 #pragma unroll
     for (int c = 0; c < TL::COPIES; ++c) {
@@ -191,34 +194,69 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(PrefillArgs a
   const int v_row = 8 * (g16 >> 1) + (r16 >> 2);       // + 16*c (+4)
   const int v_col = 16 * (g16 & 1) + 4 * (r16 & 3);    // + 32*db (elements)
 
-  if (ntiles > 0) issue_tile(0, 0);
-  for (int t = 0; t < ntiles; ++t) {
-    const int cur = t & 1;
+  auto tile_step = [&](int t, const char* Ks, char* next) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t have landed
     __syncthreads();                     // ... everyone's; and tile t-1 is fully consumed
-    if (t + 1 < ntiles) issue_tile(t + 1, cur ^ 1);
-    const char* Ks = lds + cur * TL::STAGE;
     const char* Vs = Ks + TL::BYTES;
     const int64_t k0 = (int64_t)t * kBK;
 
-    f32x16 s[2];
+    // S^T = K Q^T, operands software-pipelined: the K chunks of step kk+1
+    // are read from LDS while the two (independent) products of step kk run
+    const int kr0 = perm_row(n);  // K row of this lane in block mb: 32*mb + kr0
+    const int ksw = swz_k<D>(kr0);  // the same swizzle for both blocks (32 = 0 mod 16)
+    const char* krow = Ks + kr0 * TL::ROWB;
+    auto kread = [&](int kk, int mb) {
+      return *(const lds_bf16x8*)(krow + mb * 32 * TL::ROWB + 16 * ((2 * kk + hh) ^ ksw));
+    };
+    f32x16 s[2] = {f32x16{}, f32x16{}};
+    bf16x8 kc0 = kread(0, 0), kc1 = kread(0, 1);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb] = f32x16{};
-      const int kr = 32 * mb + perm_row(n);
-      const char* rowp = Ks + kr * TL::ROWB;
-      const int sw = swz_k<D>(kr);
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        s[mb] = mfma32(*(const lds_bf16x8*)(rowp + 16 * ((2 * kk + hh) ^ sw)), qf[kk], s[mb]);
+    for (int kk = 0; kk < NKK; ++kk) {
+      bf16x8 kn0, kn1;
+      if (kk + 1 < NKK) {
+        kn0 = kread(kk + 1, 0);
+        kn1 = kread(kk + 1, 1);
+      }
+      // (keeps the next reads above these products: sunk below them, the
+      // reads would share registers with the current operands and serialise)
+      __builtin_amdgcn_sched_barrier(0);
+      s[0] = mfma32(kc0, qf[kk], s[0]);
+      s[1] = mfma32(kc1, qf[kk], s[1]);
+      if (kk + 1 < NKK) {
+        kc0 = kn0;
+        kc1 = kn1;
+      }
     }
+
+    // V^T operand (key chunk c of 16, output rows 32*db ..) by two transposing reads
+    auto vread = [&](int c, int db) {
+      const int row = 16 * c + v_row;
+      const int col = 32 * db + v_col;
+      const char* p0 = Vs + row * TL::ROWB + 16 * ((col >> 3) ^ swz_v<D>(row)) + 2 * (col & 7);
+      const char* p1 = p0 + 4 * TL::ROWB;  // row + 4 has the same swizzle
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // all V^T operands of the tile, read before the next tile's copies are
+    // issued: a transposing LDS read issued while direct-to-LDS copies are in
+    // flight makes the compiler wait for those copies first
+    bf16x8 vt[4][NDB];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vt[c][db] = vread(c, db);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 < ntiles) issue_tile(t + 1, next);
+
     if (k0 + kBK > kfull) {  // tile reaches past the keys every row sees: mask per element
-      const int rel = (int)max(min(lim - k0, (int64_t)kBK), (int64_t)-1);  // last visible key in the tile
+      // last visible key in the tile, relative to this lane's first key (8*hh)
+      const int rel = (int)max(min(lim - k0, (int64_t)kBK), (int64_t)-1) - 8 * hh;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (32 * mb + 16 * (i >> 3) + 8 * hh + (i & 7) > rel) s[mb][i] = -INFINITY;
+          if (32 * mb + 16 * (i >> 3) + (i & 7) > rel) s[mb][i] = -INFINITY;
     }
     float tmax = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
 #pragma unroll
@@ -255,20 +293,17 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(PrefillArgs a
       }
     }
     l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    // O^T += V^T P^T
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int row = 16 * c + v_row;
-        const int col = 32 * db + v_col;
-        const char* p0 = Vs + row * TL::ROWB + 16 * ((col >> 3) ^ swz_v<D>(row)) + 2 * (col & 7);
-        const char* p1 = Vs + (row + 4) * TL::ROWB + 16 * ((col >> 3) ^ swz_v<D>(row + 4)) + 2 * (col & 7);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
-        const i16x8 v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[db] = mfma32(__builtin_bit_cast(bf16x8, v8), pf[c], acc[db]);
-      }
-    }
+      for (int db = 0; db < NDB; ++db) acc[db] = mfma32(vt[c][db], pf[c], acc[db]);
+  };
+
+  if (ntiles > 0) issue_tile(0, stage0);
+  for (int t = 0; t < ntiles; t += 2) {
+    tile_step(t, stage0, stage1);
+    if (t + 1 < ntiles) tile_step(t + 1, stage1, stage0);
   }
 
   const float lt = half_swap_sum(l);
@@ -318,18 +353,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(PrefillArgs a
 
 template <int D>
 attn_status launch_d(const PrefillArgs& a, int tiles, hipStream_t stream) {
-  static bool attr_set[64] = {false};
-  int dev = 0;
-  (void)hipGetDevice(&dev);
-  if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-    const hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, Tile<D>::LDS);
-    if (e != hipSuccess) return set_error(ATTN_E_DEVICE, "prefill_bf16: LDS attribute: %s", hipGetErrorString(e));
-    attr_set[dev] = true;
-  }
   const int64_t total = (int64_t)tiles * a.Hkv * a.B;
   if (total > 0x7fffffff) return set_error(ATTN_E_UNSUPPORTED, "prefill: too many work-groups per launch");
-  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)total), dim3(kThreads), Tile<D>::LDS, stream, a, tiles);
+  hipLaunchKernelGGL(prefill_bf16_kernel<D>, dim3((unsigned)total), dim3(kThreads), 0, stream, a, tiles);
   return check_launch("prefill_bf16");
 }
 

@@ -8,6 +8,8 @@ only unmasked (query, key) pairs at 4*D flop each.  Beside it, in the same run:
     D=128, 512-token pages, ragged lengths U[1024, 32768]) in GB/s of KV bytes
     of valid tokens (+ q, o, lse), with the cache copies rotated so each
     timed launch streams from HBM rather than from the 256 MB last-level cache;
+  * ``decode_quant``: the same decode over contiguous int8 and OCP e4m3fn
+    caches (B=4, Hq=32, Hkv=8, D=128, T=65536) in GB/s of cache bytes;
   * ``roofline`` / ``decode.roofline``: achieved vs MI355X peak, timed with HIP
     events on the stream the kernels are launched on;
   * ``cpu_baseline``: the fp64 oracle on a bounded sample of query rows of the
@@ -171,6 +173,63 @@ def bench_decode(args):
                          "traffic": recorded_traffic("decode_paged_bf16_pmc_traffic.md", "decode.hip")}}
 
 
+def bench_decode_quant(args):
+    """Quantised-cache decode (B=4, Hq=32, Hkv=8, D=128, T=65536 for every
+    sequence, contiguous cache): int8 codes with per-(token, KV head) scales,
+    and OCP e4m3fn codes with per-KV-head scales.  The codes are seeded
+    synthetic draws made on the device (parity on the same shapes is the
+    GPU test suite's job); GB/s counts the cache bytes (codes + int8 scales)."""
+    import torch
+
+    import attn_inputs as gen
+    import exact_long_context_tiled_amd as attn
+
+    w = gen.WORKLOADS["quant_decode"]
+    B, Hq, Hkv, D, T = w["B"], w["Hq"], w["Hkv"], w["D"], max(w["T"])
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0x5EED + 4)
+    q = torch.randn((B, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    ws = torch.empty(attn.decode_workspace_size(B, Hq, Hkv, D, T), dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    res = {}
+    for kv in ("int8", "fp8"):
+        shape = (B, Hkv, T, D)
+        code_bytes = B * Hkv * T * D * 2
+        copies = max(2, math.ceil((1 << 30) / code_bytes))
+        caches = []
+        for _ in range(copies):
+            if kv == "int8":
+                k = torch.randint(-127, 128, shape, generator=g, dtype=torch.int8, device="cuda")
+                v = torch.randint(-127, 128, shape, generator=g, dtype=torch.int8, device="cuda")
+                ks = torch.rand((B, Hkv, T), generator=g, device="cuda") * 0.02 + 0.005
+                vs = torch.rand((B, Hkv, T), generator=g, device="cuda") * 0.02 + 0.005
+            else:
+                k = torch.randn(shape, generator=g, device="cuda").to(torch.float8_e4m3fn)
+                v = torch.randn(shape, generator=g, device="cuda").to(torch.float8_e4m3fn)
+                ks = torch.full((Hkv,), 0.25, device="cuda")
+                vs = torch.full((Hkv,), 0.25, device="cuda")
+            caches.append((k, v, ks, vs))
+
+        def step(i, caches=caches, copies=copies):
+            k, v, ks, vs = caches[i % copies]
+            attn.decode_splitkv(q, k, v, lens, T, k_scale=ks, v_scale=vs, workspace=ws, out=o, lse=lse)
+
+        steps = max(args.steps, copies * 4)
+        ms = timed(step, steps, max(args.warmup, copies), stream)
+        nbytes = code_bytes + (B * Hkv * T * 4 * 2 if kv == "int8" else 0)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"decode {kv}: {ms * 1e3:.2f} us/call, {gbs:.1f} GB/s ({nbytes / 1e6:.1f} MB)")
+        res[kv] = {"value": round(gbs, 2), "unit": "GB/s", "us_per_call": round(ms * 1e3, 3), "bytes": nbytes,
+                   "cache_copies": copies, "steps": steps,
+                   "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+        del caches
+    return {"workload": "quant_decode", "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "T": T, "kv": res}
+
+
 def cpu_baseline(case, w, target_s):
     import oracle
     import attn_inputs as gen
@@ -265,6 +324,7 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = bench_decode(args)
+        out["decode_quant"] = bench_decode_quant(args)
     if args.stream:
         out["stream"] = bench_stream(args)
     if args.calibrate_copy:

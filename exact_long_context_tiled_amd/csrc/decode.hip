@@ -26,13 +26,15 @@
 // This is a bandwidth-bound scan, so the vector ALUs do the arithmetic.  The
 // lanes of a wave form token slots of D*bytes/16 lanes, each lane owning one
 // 16-byte slice of a token's K and V rows; every iteration a wave loads the K
-// and V slices of U tokens per slot (all loads in flight together), reduces
+// and V slices of 4 tokens per slot (all loads in flight together), reduces
 // the slice dot products across the slot with row-local DPP moves, and
 // folds the tokens into a per-slot online softmax (running max, sum and
-// output accumulator).  bf16 K is dotted with the exact bf16 query in packed
-// bf16 pairs; int8 / fp8 slices are converted to fp32.  At the end of a piece
-// the slots of a wave, then the waves of the work-group, are combined by the same
-// max/rescale rule.  Pieces start on 16-token group boundaries and pages hold
+// output accumulator).  K slices of every type are turned into exact bf16
+// pairs (e4m3 and int8 values are all bf16 numbers) and dotted with the exact
+// bf16 query by the packed bf16 dot product; V slices are converted to fp32
+// for the fp32 P.V accumulation.  At the end of a piece the slots of a wave,
+// then the waves of the work-group, are combined by the same max/rescale
+// rule.  Pieces start on 16-token group boundaries and pages hold
 // a power-of-two number >= 16 of tokens, so the tokens of one wave load step
 // never straddle a page and its page-table entry is one scalar read.
 #include <math.h>
@@ -102,6 +104,36 @@ __device__ __forceinline__ float token_sum(float x) {
 }
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// One 16-byte K slice as EPL/2 exact bf16 pairs, the operand of the packed
+// bf16 dot product: every e4m3fn value and every int8 code is a bf16 number.
+// e4m3fn goes through gfx950's scaled fp8 -> bf16 pair conversion (scale 1);
+// int8 through fp32, whose upper half is then the exact bf16.
+template <int KV>
+__device__ __forceinline__ void k_pairs(uint4 raw, bf16x2* out) {
+  const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+  if constexpr (KV == ATTN_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __builtin_bit_cast(bf16x2, wd[i]);
+  } else if constexpr (KV == ATTN_FP8_E4M3) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd[i], 1.0f, false);
+      out[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd[i], 1.0f, true);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const float f0 = (float)(int)(int8_t)(wd[i] >> (16 * hf));
+        const float f1 = (float)(int)(int8_t)(wd[i] >> (16 * hf + 8));
+        out[2 * i + hf] = __builtin_bit_cast(
+            bf16x2, __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u));
+      }
+    }
+  }
+}
 
 // {a, b} = {x of this lane, x of lane ^ OFF} in a lane-fixed order (the
 // combine below is symmetric in the two): one permlane swap for OFF = 32 or
@@ -188,9 +220,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
   constexpr int EPL = 16 / EB;   // elements per lane slice
   constexpr int LPT = D / EPL;   // lanes per token
   constexpr int TPW = 64 / LPT;  // tokens per wave per load step (token slots)
-  constexpr int U = EB == 2 ? 4 : 2;  // load steps per iteration (16 tokens per wave at D = 128)
+  constexpr int U = 4;           // load steps per iteration
   constexpr int TPI = TPW * U;   // tokens per wave per iteration
-  constexpr bool kDot2 = KV == ATTN_BF16;
   constexpr int REC = G * D + 16;
   static_assert(kDecodeGroup % TPW == 0, "a load step must not straddle a group");
   extern __shared__ int64_t pre[];  // [B + 1]
@@ -237,11 +268,11 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
     const bool whole = j0 == 0 && pend == seg_end;
     const int64_t row0 = (int64_t)b * a.Hq + (int64_t)hk * G;  // first (b, h) row of this group
 
-    // query slices: exact bf16 pairs for the packed dot (bf16 cache), or fp32
-    // pre-multiplied by scale*log2(e) (and the fp8 per-head K scale)
-    bf16x2 q2[kDot2 ? G : 1][kDot2 ? EPL / 2 : 1];
-    float qf[kDot2 ? 1 : G][kDot2 ? 1 : EPL];
+    // query slices as exact bf16 pairs for the packed dot product; the score
+    // multiplier carries scale*log2(e) (and the e4m3 per-head K scale)
+    bf16x2 q2[G][EPL / 2];
     float smul = a.scale_log2;
+    if constexpr (KV == ATTN_FP8_E4M3) smul *= a.k_scale[hk];
     {
       const uint16_t* qb = (const uint16_t*)a.q + row0 * D + part * EPL;
 #pragma unroll
@@ -249,21 +280,11 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
 #pragma unroll
         for (int e = 0; e < EPL; e += 8) {
           const uint4 raw = *(const uint4*)(qb + (int64_t)g * D + e);
-          if constexpr (kDot2) {
-            const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+          const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) q2[g][e / 2 + i] = __builtin_bit_cast(bf16x2, wd[i]);
-          } else {
-            float tmp[8];
-            decode16<ATTN_BF16>(raw, tmp);
-            float qmul = a.scale_log2;
-            if constexpr (KV == ATTN_FP8_E4M3) qmul *= a.k_scale[hk];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) qf[g][e + i] = tmp[i] * qmul;
-          }
+          for (int i = 0; i < 4; ++i) q2[g][e / 2 + i] = __builtin_bit_cast(bf16x2, wd[i]);
         }
       }
-      if constexpr (!kDot2) smul = 1.f;
     }
 
     float m[G], l[G], acc[G][EPL];
@@ -324,26 +345,14 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
       float s[U][G];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        if constexpr (kDot2) {
-          const uint32_t wd[4] = {bf.kr[u].x, bf.kr[u].y, bf.kr[u].z, bf.kr[u].w};
+        bf16x2 kp[EPL / 2];
+        k_pairs<KV>(bf.kr[u], kp);
 #pragma unroll
-          for (int g = 0; g < G; ++g) {
-            float d = 0.f;
+        for (int g = 0; g < G; ++g) {
+          float d = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              d = __builtin_amdgcn_fdot2_f32_bf16(q2[g][i], __builtin_bit_cast(bf16x2, wd[i]), d, false);
-            s[u][g] = d;
-          }
-        } else {
-          float kv[EPL];
-          decode16<KV>(bf.kr[u], kv);
-#pragma unroll
-          for (int g = 0; g < G; ++g) {
-            float d = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e) d = fmaf(qf[g][e], kv[e], d);
-            s[u][g] = d;
-          }
+          for (int i = 0; i < EPL / 2; ++i) d = __builtin_amdgcn_fdot2_f32_bf16(q2[g][i], kp[i], d, false);
+          s[u][g] = d;
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {

@@ -225,7 +225,8 @@ def bench_decode_quant(args):
         res[kv] = {"value": round(gbs, 2), "unit": "GB/s", "us_per_call": round(ms * 1e3, 3), "bytes": nbytes,
                    "cache_copies": copies, "steps": steps,
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+                                "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                "traffic": recorded_traffic(f"decode_{kv}_contig_pmc_traffic.md", "decode.hip")}}
         del caches
     return {"workload": "quant_decode", "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "T": T, "kv": res}
 

@@ -15,7 +15,9 @@ only unmasked (query, key) pairs at 4*D flop each.  Beside it, in the same run:
   * ``cpu_baseline``: the fp64 oracle on a bounded sample of query rows of the
     same prefill workload, on this host's cores.
 ``--stream`` adds one run of the budgeted streaming prefill (B=1, Hq=32, Hkv=8,
-S=T=2^20, D=128, bf16, 4 GB device budget) from pinned host memory.
+S=T=2^20, D=128, bf16, 4 GB device budget) from pinned host memory;
+``--stream-cqs`` runs the same workload with the cyclic-quorum plan (and, with
+``--stream``, compares the two outputs).
 
 Prints ONE JSON line.  Inputs are seeded synthetic N(0,1) data.
 """
@@ -273,13 +275,31 @@ def bench_stream(args):
     gen.normal(hk.shape, seed, gen.TID_K, "bf16", out=hk.numpy().view(np.uint16))
     gen.normal(hv.shape, seed, gen.TID_V, "bf16", out=hv.numpy().view(np.uint16))
     log(f"stream: inputs generated in {time.perf_counter() - t0:.1f} s")
-    o, lse, rep = attn.stream_budgeted(hq.view(torch.bfloat16), hk.view(torch.bfloat16), hv.view(torch.bfloat16),
-                                       causal=True, scale=1 / math.sqrt(D), budget=w["budget"])
+    qb, kb, vb = hq.view(torch.bfloat16), hk.view(torch.bfloat16), hv.view(torch.bfloat16)
     flops = 4.0 * D * B * Hq * (S * (S + 1) // 2)
-    log(f"stream: {rep}")
-    return {"workload": "stream_cqsa_causal_1m", "budget_bytes": w["budget"], "report": rep,
-            "tflops_end_to_end": round(flops / rep["wall_s"] / 1e12, 2),
-            "tflops_kernels": round(flops / rep["kernel_s"] / 1e12, 2)}
+    out = {"workload": "stream_cqsa_causal_1m", "budget_bytes": w["budget"]}
+
+    def rates(rep):
+        return {"report": rep, "tflops_end_to_end": round(flops / rep["wall_s"] / 1e12, 2),
+                "tflops_kernels": round(flops / rep["kernel_s"] / 1e12, 2),
+                "host_link_gbs": round((rep["h2d_bytes"] + rep["d2h_bytes"]) / rep["wall_s"] / 1e9, 2)}
+
+    o_r = None
+    if args.stream:
+        o_r, _, rep = attn.stream_budgeted(qb, kb, vb, causal=True, scale=1 / math.sqrt(D), budget=w["budget"])
+        log(f"stream (rectangular): {rep}")
+        out.update(rates(rep))
+    if args.stream_cqs:
+        o_c, _, info, rep = attn.stream_cqs(qb, kb, vb, causal=True, scale=1 / math.sqrt(D), budget=w["budget"])
+        log(f"stream (cyclic quorums): N={info['n_blocks']} k={info['quorum_size']} {rep}")
+        out["cqs"] = dict(rates(rep), n_blocks=info["n_blocks"], quorum_size=info["quorum_size"],
+                          pairs=info["pairs"])
+        if o_r is not None:  # both plans compute the same exact attention
+            step = 1 << 16
+            diff = max(float((o_r[:, s0:s0 + step] - o_c[:, s0:s0 + step]).abs().max()) for s0 in range(0, S, step))
+            out["cqs"]["max_abs_diff_vs_rectangular"] = diff
+            log(f"stream: cyclic-quorum vs rectangular output max |diff| = {diff:.3e}")
+    return out
 
 
 def main():
@@ -291,6 +311,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--stream", action="store_true", help="also run the 2^20-token budgeted streaming workload")
+    ap.add_argument("--stream-cqs", action="store_true",
+                    help="also run that workload with the cyclic-quorum plan (host-link heavy: minutes)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device-to-device copy three times (PMC byte-counter reference)")
     args = ap.parse_args()
@@ -326,7 +348,7 @@ def main():
     if not args.no_decode:
         out["decode"] = bench_decode(args)
         out["decode_quant"] = bench_decode_quant(args)
-    if args.stream:
+    if args.stream or args.stream_cqs:
         out["stream"] = bench_stream(args)
     if args.calibrate_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)

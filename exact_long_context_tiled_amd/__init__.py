@@ -22,10 +22,12 @@ from ._binding import (  # noqa: F401
     merge_partials,
     prefill,
     stream_budgeted,
+    stream_cqs,
+    stream_cqs_plan,
     stream_plan,
 )
 
 __all__ = [
     "AttnError", "prefill", "decode_splitkv", "decode_workspace_size", "merge_partials", "stream_budgeted",
-    "stream_plan", "last_error", "lib", "lib_path",
+    "stream_plan", "stream_cqs", "stream_cqs_plan", "last_error", "lib", "lib_path",
 ]

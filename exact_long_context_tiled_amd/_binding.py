@@ -29,6 +29,15 @@ class StreamReport(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class CqsInfo(ctypes.Structure):
+    _fields_ = [("n_blocks", ctypes.c_int64), ("quorum_size", ctypes.c_int64), ("pairs", ctypes.c_int64),
+                ("base", ctypes.c_int64 * 128)]
+
+    def as_dict(self):
+        return {"n_blocks": self.n_blocks, "quorum_size": self.quorum_size, "pairs": self.pairs,
+                "base": list(self.base[:self.quorum_size])}
+
+
 _lib = None
 
 
@@ -58,6 +67,12 @@ def lib():
         L.attn_stream_plan.argtypes = [I, I, I, I, I64, I64, I, I, SZ, I64, I64, P, I64,
                                        ctypes.POINTER(StreamReport)]
         L.attn_stream_plan.restype = I
+        L.attn_stream_cqs.argtypes = [I, P, P, P, I, I, I, I64, I64, I, I, F, SZ, I64, P, P,
+                                      ctypes.POINTER(CqsInfo), ctypes.POINTER(StreamReport)]
+        L.attn_stream_cqs.restype = I
+        L.attn_stream_cqs_plan.argtypes = [I, I, I, I, I64, I64, I, I, SZ, I64, P, I64, ctypes.POINTER(CqsInfo),
+                                           ctypes.POINTER(StreamReport)]
+        L.attn_stream_cqs_plan.restype = I
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -200,3 +215,44 @@ def stream_plan(dtype, B, Hq, Hkv, S, T, D, *, causal=True, budget, block_q=0, b
                                       tasks.ctypes.data_as(ctypes.c_void_p), rep.tasks, ctypes.byref(rep)))
         tasks = tasks[:rep.tasks]
     return tasks, rep.as_dict()
+
+
+def stream_cqs(q_host, k_host, v_host, *, causal=True, scale=None, budget, n_blocks=0, o_host=None, lse_host=None,
+               return_lse=True):
+    """Budgeted streaming prefill over cyclic quorums (synchronous).  Arguments
+    as stream_budgeted; n_blocks 0 = chosen from the budget.
+    Returns (o_host, lse_host or None, info dict, report dict)."""
+    for t, n in ((q_host, "q_host"), (k_host, "k_host"), (v_host, "v_host")):
+        _need(t, n, device=False)
+    B, S, Hq, D = q_host.shape
+    T, Hkv = k_host.shape[1], k_host.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if o_host is None:
+        o_host = torch.empty((B, S, Hq, D), dtype=torch.float32, pin_memory=True)
+    if lse_host is None and return_lse:
+        lse_host = torch.empty((B, Hq, S), dtype=torch.float32, pin_memory=True)
+    info, rep = CqsInfo(), StreamReport()
+    _check(lib().attn_stream_cqs(_dt(q_host), _ptr(q_host), _ptr(k_host), _ptr(v_host), B, Hq, Hkv, S, T, D,
+                                 int(causal), scale, int(budget), int(n_blocks), _ptr(o_host), _ptr(lse_host),
+                                 ctypes.byref(info), ctypes.byref(rep)))
+    return o_host, lse_host, info.as_dict(), rep.as_dict()
+
+
+def stream_cqs_plan(dtype, B, Hq, Hkv, S, T, D, *, causal=True, budget, n_blocks=0, with_pairs=True):
+    """The plan stream_cqs would run (host only).  Returns (pairs int64 [n,4] of
+    (b, quorum, q block, k block; -1 = empty) or None, info dict, report dict)."""
+    import numpy as np
+
+    dt = {"bf16": ATTN_BF16, "f32": ATTN_F32}.get(dtype, dtype)
+    info, rep = CqsInfo(), StreamReport()
+    _check(lib().attn_stream_cqs_plan(dt, B, Hq, Hkv, S, T, D, int(causal), int(budget), int(n_blocks), None, 0,
+                                      ctypes.byref(info), ctypes.byref(rep)))
+    pairs = None
+    if with_pairs:
+        pairs = np.zeros((max(info.pairs, 1), 4), dtype=np.int64)
+        _check(lib().attn_stream_cqs_plan(dt, B, Hq, Hkv, S, T, D, int(causal), int(budget), int(n_blocks),
+                                          pairs.ctypes.data_as(ctypes.c_void_p), info.pairs, ctypes.byref(info),
+                                          ctypes.byref(rep)))
+        pairs = pairs[:info.pairs]
+    return pairs, info.as_dict(), rep.as_dict()

@@ -29,14 +29,90 @@
 #include <vector>
 
 #include "common.h"
+#include "stream_common.h"
 
 namespace attn {
 
+namespace streamx {
+
+attn_status check_stream_sizes(attn_dtype dt, int B, int Hq, int Hkv, int64_t S, int64_t T, int D) {
+  if (dt != ATTN_BF16 && dt != ATTN_F32) return set_error(ATTN_E_UNSUPPORTED, "stream: dtype must be bf16 or f32");
+  if (D != 64 && D != 128) return set_error(ATTN_E_UNSUPPORTED, "stream: D must be 64 or 128 (got %d)", D);
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || S < 0 || T < 0)
+    return set_error(ATTN_E_INVALID, "stream: invalid sizes");
+  return ATTN_OK;
+}
+
+namespace {
+bool is_pinned_host(const void* p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return attr.type == hipMemoryTypeHost;
+}
+}  // namespace
+
+attn_status check_pinned(attn_dtype dt, const void* q, const void* k, const void* v, const float* o,
+                         const float* lse, int B, int Hq, int Hkv, int64_t S, int64_t T, int D) {
+  const int64_t es = elem_size(dt);
+  struct {
+    const void* p;
+    int64_t bytes;
+    const char* name;
+  } hb[] = {{q, (int64_t)B * S * Hq * D * es, "q"},
+            {k, (int64_t)B * T * Hkv * D * es, "k"},
+            {v, (int64_t)B * T * Hkv * D * es, "v"},
+            {o, (int64_t)B * S * Hq * D * 4, "o"},
+            {lse, (int64_t)B * Hq * S * 4, "lse"}};
+  for (auto& h : hb) {
+    if (!h.p || h.bytes == 0) continue;
+    if (!is_pinned_host(h.p) || !is_pinned_host((const char*)h.p + h.bytes - 1))
+      return set_error(ATTN_E_INVALID, "stream: host buffer %s is not pinned host memory", h.name);
+  }
+  return ATTN_OK;
+}
+
+PrefillArgs block_args(const void* q, const void* k, const void* v, float* o, float* lse, int Hq, int Hkv, int D,
+                       int64_t n_q, int64_t n_k, int64_t q_abs0, int64_t k_abs0, int causal, int accumulate,
+                       float scale_log2) {
+  PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.q_sb = 0;
+  a.q_ss = (int64_t)Hq * D;
+  a.k_sb = 0;
+  a.k_ss = (int64_t)Hkv * D;
+  a.o_sb = 0;
+  a.o_ss = (int64_t)Hq * D;
+  a.l_sb = 0;
+  a.l_sh = n_q;
+  a.n_q = n_q;
+  a.n_k = n_k;
+  a.q_abs0 = q_abs0;
+  a.k_abs0 = k_abs0;
+  a.B = 1;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = Hq / Hkv;
+  a.causal = causal;
+  a.accumulate = accumulate;
+  a.scale_log2 = scale_log2;
+  return a;
+}
+
+}  // namespace streamx
+
 namespace {
 
-constexpr int64_t kAlign = 256;
-constexpr int64_t kAllocSlack = 2ll << 20;  // device allocation granularity
-int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+using streamx::align_up;
+using streamx::elem_size;
+using streamx::kAlign;
+using streamx::kAllocSlack;
 
 struct Plan {
   int64_t bq = 0, bk = 0;
@@ -45,8 +121,6 @@ struct Plan {
   int64_t device_bytes = 0;
   int64_t tasks = 0, h2d = 0, d2h = 0;
 };
-
-int64_t elem_size(attn_dtype dt) { return dt == ATTN_F32 ? 4 : 2; }
 
 // Key blocks visible to query block qb: [0, count).  0 means "no key at all".
 int64_t visible_kblocks(const Plan& p, int64_t qb, int64_t S, int64_t T, int causal) {
@@ -98,7 +172,7 @@ attn_status make_plan(attn_dtype dt, int B, int Hq, int Hkv, int64_t S, int64_t 
                       size_t budget, int64_t force_q, int64_t force_k, Plan* out) {
   // keep room for the allocator's rounding of the one arena allocation
   const int64_t raw = budget > (size_t)INT64_MAX ? INT64_MAX : (int64_t)budget;
-  const int64_t bud = raw - kAllocSlack;
+  const int64_t bud = streamx::usable_budget(budget);
   const int64_t tq = std::max<int64_t>(T, 1);
   auto try_plan = [&](int64_t bq, int64_t bk, Plan* p) {
     p->bq = bq;
@@ -150,15 +224,6 @@ attn_status make_plan(attn_dtype dt, int B, int Hq, int Hkv, int64_t S, int64_t 
   return ATTN_OK;
 }
 
-bool is_pinned_host(const void* p) {
-  hipPointerAttribute_t attr;
-  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
-    (void)hipGetLastError();
-    return false;
-  }
-  return attr.type == hipMemoryTypeHost;
-}
-
 }  // namespace
 
 }  // namespace attn
@@ -168,16 +233,15 @@ using namespace attn;
 extern "C" attn_status attn_stream_plan(attn_dtype dt, int B, int Hq, int Hkv, int64_t S, int64_t T, int D,
                                         int causal, size_t device_budget_bytes, int64_t block_q, int64_t block_k,
                                         int64_t* tasks, int64_t cap, attn_stream_report* plan) {
-  if (dt != ATTN_BF16 && dt != ATTN_F32) return set_error(ATTN_E_UNSUPPORTED, "stream: dtype must be bf16 or f32");
-  if (D != 64 && D != 128) return set_error(ATTN_E_UNSUPPORTED, "stream: D must be 64 or 128 (got %d)", D);
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || S < 0 || T < 0 || block_q < 0 || block_k < 0 || cap < 0)
-    return set_error(ATTN_E_INVALID, "stream: invalid sizes");
+  attn_status st = streamx::check_stream_sizes(dt, B, Hq, Hkv, S, T, D);
+  if (st != ATTN_OK) return st;
+  if (block_q < 0 || block_k < 0 || cap < 0) return set_error(ATTN_E_INVALID, "stream: invalid sizes");
   Plan p;
   if (B == 0 || S == 0) {
     if (plan) memset(plan, 0, sizeof(*plan));
     return ATTN_OK;
   }
-  attn_status st = make_plan(dt, B, Hq, Hkv, S, T, D, causal, device_budget_bytes, block_q, block_k, &p);
+  st = make_plan(dt, B, Hq, Hkv, S, T, D, causal, device_budget_bytes, block_q, block_k, &p);
   if (st != ATTN_OK) return st;
   if (tasks) {
     int64_t n = 0;
@@ -212,10 +276,9 @@ extern "C" attn_status attn_stream_budgeted(attn_dtype dt, const void* q_host, c
                                             int64_t block_k, float* o_host, float* lse_host,
                                             attn_stream_report* report) {
   const auto wall0 = std::chrono::steady_clock::now();
-  if (dt != ATTN_BF16 && dt != ATTN_F32) return set_error(ATTN_E_UNSUPPORTED, "stream: dtype must be bf16 or f32");
-  if (D != 64 && D != 128) return set_error(ATTN_E_UNSUPPORTED, "stream: D must be 64 or 128 (got %d)", D);
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || S < 0 || T < 0 || block_q < 0 || block_k < 0)
-    return set_error(ATTN_E_INVALID, "stream: invalid sizes");
+  attn_status st = streamx::check_stream_sizes(dt, B, Hq, Hkv, S, T, D);
+  if (st != ATTN_OK) return st;
+  if (block_q < 0 || block_k < 0) return set_error(ATTN_E_INVALID, "stream: invalid sizes");
   if (!std::isfinite(scale)) return set_error(ATTN_E_INVALID, "stream: scale must be finite");
   if (B == 0 || S == 0) {
     if (report) memset(report, 0, sizeof(*report));
@@ -225,22 +288,10 @@ extern "C" attn_status attn_stream_budgeted(attn_dtype dt, const void* q_host, c
     return set_error(ATTN_E_INVALID, "stream: null host pointer");
   const int64_t es = elem_size(dt);
   // every host buffer must be pinned (page-locked, device-mapped) memory
-  struct {
-    const void* p;
-    int64_t bytes;
-    const char* name;
-  } hb[] = {{q_host, (int64_t)B * S * Hq * D * es, "q"},
-            {k_host, (int64_t)B * T * Hkv * D * es, "k"},
-            {v_host, (int64_t)B * T * Hkv * D * es, "v"},
-            {o_host, (int64_t)B * S * Hq * D * 4, "o"},
-            {lse_host, (int64_t)B * Hq * S * 4, "lse"}};
-  for (auto& h : hb) {
-    if (!h.p || h.bytes == 0) continue;
-    if (!is_pinned_host(h.p) || !is_pinned_host((const char*)h.p + h.bytes - 1))
-      return set_error(ATTN_E_INVALID, "stream: host buffer %s is not pinned host memory", h.name);
-  }
+  st = streamx::check_pinned(dt, q_host, k_host, v_host, o_host, lse_host, B, Hq, Hkv, S, T, D);
+  if (st != ATTN_OK) return st;
   Plan p;
-  attn_status st = make_plan(dt, B, Hq, Hkv, S, T, D, causal, device_budget_bytes, block_q, block_k, &p);
+  st = make_plan(dt, B, Hq, Hkv, S, T, D, causal, device_budget_bytes, block_q, block_k, &p);
   if (st != ATTN_OK) return st;
 
   // ---- resources
@@ -306,27 +357,8 @@ extern "C" attn_status attn_stream_budgeted(attn_dtype dt, const void* q_host, c
         ATTN_HIP(hipStreamWaitEvent(s_cmp, ev_q[s], 0));
         const int64_t nv = visible_kblocks(p, qb, S, T, causal);
         for (int64_t kb = 0; kb < std::max<int64_t>(nv, 1); ++kb) {
-          PrefillArgs a{};
-          a.q = qbuf[s];
-          a.o = (float*)obuf[s];
-          a.lse = (float*)lbuf[s];
-          a.q_sb = 0;
-          a.q_ss = (int64_t)Hq * D;
-          a.k_sb = 0;
-          a.k_ss = (int64_t)Hkv * D;
-          a.o_sb = 0;
-          a.o_ss = (int64_t)Hq * D;
-          a.l_sb = 0;
-          a.l_sh = nq;
-          a.n_q = nq;
-          a.q_abs0 = q0 + (T - S);
-          a.B = 1;
-          a.Hq = Hq;
-          a.Hkv = Hkv;
-          a.G = Hq / Hkv;
-          a.causal = causal;
-          a.accumulate = kb > 0;
-          a.scale_log2 = scale_log2;
+          PrefillArgs a = streamx::block_args(qbuf[s], nullptr, nullptr, (float*)obuf[s], (float*)lbuf[s], Hq, Hkv,
+                                              D, nq, 0, q0 + (T - S), 0, causal, kb > 0, scale_log2);
           if (nv == 0) {  // no visible key: an empty key block writes O = 0, lse = -inf
             a.k = a.v = qbuf[s];
             a.n_k = 0;

@@ -195,6 +195,61 @@ attn_status attn_stream_plan(attn_dtype dt, int B, int Hq, int Hkv, int64_t S, i
                              size_t device_budget_bytes, int64_t block_q, int64_t block_k, int64_t* tasks,
                              int64_t cap, attn_stream_report* plan);
 
+/* Cyclic-quorum plan facts (attn_stream_cqs / attn_stream_cqs_plan). */
+#define ATTN_CQS_MAX_QUORUM 128
+typedef struct attn_cqs_info {
+  int64_t n_blocks;    /* N: blocks per sequence, on the query and on the key side alike */
+  int64_t quorum_size; /* k: blocks per quorum */
+  int64_t pairs;       /* (query block, key block) pairs computed, all sequences, empty ones included */
+  int64_t base[ATTN_CQS_MAX_QUORUM]; /* base quorum D (first quorum_size entries, ascending, D[0] = 0) */
+} attn_cqs_info;
+
+/*
+ * Budgeted streaming prefill decomposed by cyclic quorums (the CQS Divide:
+ * Stream-CQSA summary, "Methodology" items 1-3).  Query positions and key
+ * positions are each cut into N blocks (block x: queries
+ * [x*block_q, (x+1)*block_q), keys [x*block_k, (x+1)*block_k)).  The base
+ * quorum D is a planar difference set modulo N -- every nonzero residue is a
+ * difference of exactly one ordered pair of D -- and quorum i = D + i (mod N)
+ * is one sub-task per sequence: it loads the Q/K/V blocks of its k members
+ * and computes the (query block x, key block y) pairs with x - y a difference
+ * d_a - d_b of members (x = d_a + i); the diagonal (x, x) belongs to quorum x.
+ * So every pair is computed exactly once (causally invisible pairs are
+ * skipped), and the pair results are merged exactly by log-sum-exp into each
+ * query block's running (O, lse), which is swapped out to o_host / lse_host
+ * between sub-tasks.  The textbook cyclic-quorum construction (Singer
+ * difference sets) is the reading taken where the page gives none.
+ *
+ *   Arguments as attn_stream_budgeted, except:
+ *   n_blocks   0 = the smallest supported N whose two double-buffered
+ *              sub-task slots fit device_budget_bytes; else N, one of 1, 3
+ *              or p*p + p + 1 for a prime p <= 127 (quorum sizes 1, 2, p + 1)
+ *   lse_host   may be NULL: the running lse then lives in a pinned host
+ *              buffer the call allocates and frees
+ *   info       NULL or filled with N, k, the pair count and D on success
+ * report->tasks counts the quorum sub-tasks that hold at least one pair.
+ * Synchronous; uses the current HIP device; every device byte it allocates is
+ * freed before return.
+ * Errors: ATTN_E_INVALID (incl. non-pinned host memory), ATTN_E_UNSUPPORTED
+ * (dt, D, an n_blocks with no difference set), ATTN_E_BUDGET, ATTN_E_DEVICE.
+ */
+attn_status attn_stream_cqs(attn_dtype dt, const void* q_host, const void* k_host, const void* v_host, int B, int Hq,
+                            int Hkv, int64_t S, int64_t T, int D, int causal, float scale,
+                            size_t device_budget_bytes, int64_t n_blocks, float* o_host, float* lse_host,
+                            attn_cqs_info* info, attn_stream_report* report);
+
+/*
+ * The plan attn_stream_cqs would execute, on the host only (no device
+ * access).  pairs (nullable) receives up to cap quadruples (sequence b,
+ * quorum index i, query block x, key block y) in execution order, with
+ * y = -1 for the empty pair of a query block that sees no key; info and plan
+ * (nullable) receive the plan facts and counters (wall_s = kernel_s = 0).
+ * Errors: ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_BUDGET.
+ */
+attn_status attn_stream_cqs_plan(attn_dtype dt, int B, int Hq, int Hkv, int64_t S, int64_t T, int D, int causal,
+                                 size_t device_budget_bytes, int64_t n_blocks, int64_t* pairs, int64_t cap,
+                                 attn_cqs_info* info, attn_stream_report* plan);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* attn_last_error(void);
 

@@ -24,7 +24,8 @@ def test_library_exports_every_declared_symbol():
     L = attn.lib()
     syms = _declared_symbols()
     assert set(syms) >= {"attn_prefill", "attn_decode_splitkv", "attn_merge_partials", "attn_stream_budgeted",
-                         "attn_stream_plan", "attn_decode_workspace_size", "attn_last_error"}
+                         "attn_stream_plan", "attn_decode_workspace_size", "attn_last_error", "attn_stream_cqs",
+                         "attn_stream_cqs_plan"}
     for s in syms:
         assert hasattr(L, s), s
 

@@ -343,10 +343,11 @@ def test_stream_budget_too_small_fails_before_allocating():
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
-def test_stream_cqsa_million_token_causal():
+@pytest.mark.parametrize("plan", ["rectangular", "cyclic_quorum"])
+def test_stream_cqsa_million_token_causal(plan):
     """B=1 Hq=32 Hkv=8 S=T=2^20 D=128 bf16 causal from pinned host memory under a 4 GB
-    device budget: checked against the unbudgeted on-device run on every output and
-    against the fp64 oracle on 64 seeded query rows x all heads."""
+    device budget, with either plan: checked against the unbudgeted on-device run on
+    every output and against the fp64 oracle on 64 seeded query rows x all heads."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
@@ -366,12 +367,18 @@ def test_stream_cqsa_million_token_causal():
     with ThreadPoolExecutor(max_workers=1) as ex:
         fut = ex.submit(oracle.attention, qn, kn, vn, B=B, Hq=Hq, Hkv=Hkv, S=S, T=T, D=D, causal=True,
                         scale=scale, rows=rows)
-        o_h, lse_h, rep = attn.stream_budgeted(hq.view(torch.bfloat16), hk.view(torch.bfloat16),
-                                               hv.view(torch.bfloat16), causal=True, scale=scale,
-                                               budget=w["budget"])
-        say(f"stream 1M: {rep}")
+        if plan == "rectangular":
+            o_h, lse_h, rep = attn.stream_budgeted(hq.view(torch.bfloat16), hk.view(torch.bfloat16),
+                                                   hv.view(torch.bfloat16), causal=True, scale=scale,
+                                                   budget=w["budget"])
+            assert rep["d2h_bytes"] == S * Hq * D * 4 + S * Hq * 4
+        else:
+            o_h, lse_h, info, rep = attn.stream_cqs(hq.view(torch.bfloat16), hk.view(torch.bfloat16),
+                                                    hv.view(torch.bfloat16), causal=True, scale=scale,
+                                                    budget=w["budget"])
+            assert info["pairs"] == info["n_blocks"] * (info["n_blocks"] + 1) // 2
+        say(f"stream 1M {plan}: {rep}")
         assert rep["peak_device_bytes"] <= w["budget"]
-        assert rep["d2h_bytes"] == S * Hq * D * 4 + S * Hq * 4
         # the unbudgeted run, all on the device
         od, ld = attn.prefill(hq.view(torch.bfloat16).cuda(), hk.view(torch.bfloat16).cuda(),
                               hv.view(torch.bfloat16).cuda(), causal=True, scale=scale)
@@ -392,3 +399,68 @@ def test_stream_cqsa_million_token_causal():
     o_s = o_h.numpy()[:, rows]
     l_s = lse_h.numpy()[:, :, rows]
     check_lp(o_s, l_s, ro, rl, "stream 1M sampled rows")
+
+
+# ------------------------------------------------------------------ cyclic-quorum streaming
+@pytest.mark.parametrize("kind,causal,S,T,n", [("bf16", True, 1000, 1000, 7), ("f32", True, 1000, 1000, 13),
+                                               ("bf16", False, 700, 900, 13), ("bf16", True, 900, 500, 7),
+                                               ("bf16", True, 500, 900, 31), ("f32", False, 333, 333, 3)])
+def test_stream_cqs_small(kind, causal, S, T, n):
+    """Cyclic-quorum streaming == oracle and == the unbudgeted device run;
+    repeatable bit for bit; without lse_host the output is unchanged."""
+    import oracle
+    B, Hq, Hkv, D = 2, 8, 2, 128
+    case = gen.prefill_inputs(B, Hq, Hkv, S, T, D, kind=kind, seed=43 + n)
+    qh, kh, vh = (_pinned(case[c]) for c in "qkv")
+    o_dev, l_dev = gpu_prefill(case, causal=causal)
+    ro, rl = oracle.prefill(case, causal=causal)
+    say(f"stream_cqs {kind} causal={causal} S={S} T={T} N={n}")
+    o, lse, info, rep = attn.stream_cqs(qh, kh, vh, causal=causal, scale=case["scale"], budget=1 << 30, n_blocks=n)
+    say(f"  info={ {k: v for k, v in info.items() if k != 'base'} } report={rep}")
+    assert info["n_blocks"] == n and rep["peak_device_bytes"] <= 1 << 30
+    o, lse = o.numpy().copy(), lse.numpy().copy()
+    if kind == "f32":
+        check_f32(o, lse, ro, rl, f"stream_cqs f32 N={n}")
+    else:
+        check_lp(o, lse, ro, rl, f"stream_cqs bf16 N={n}")
+    tol = 1e-5 if kind == "f32" else 5e-3
+    assert max_abs_err(o, o_dev) <= tol and lse_err(lse, l_dev) <= (1e-4 if kind == "f32" else 1e-3)
+    o2, lse2, _, _ = attn.stream_cqs(qh, kh, vh, causal=causal, scale=case["scale"], budget=1 << 30, n_blocks=n)
+    assert np.array_equal(o2.numpy(), o) and np.array_equal(lse2.numpy(), lse)
+    o3, none, _, _ = attn.stream_cqs(qh, kh, vh, causal=causal, scale=case["scale"], budget=1 << 30, n_blocks=n,
+                                     return_lse=False)
+    assert none is None and np.array_equal(o3.numpy(), o)
+
+
+def test_stream_cqs_budget_picks_quorums_and_matches_rectangular():
+    """Under a budget that forces N > 1 the automatic plan fits, and its output
+    equals the rectangular streaming plan's within bf16 merge rounding."""
+    B, Hq, Hkv, S, T, D = 1, 8, 2, 3000, 3000, 128
+    case = gen.prefill_inputs(B, Hq, Hkv, S, T, D, kind="bf16", seed=77)
+    qh, kh, vh = (_pinned(case[c]) for c in "qkv")
+    budget = 24 << 20
+    o, lse, info, rep = attn.stream_cqs(qh, kh, vh, causal=True, scale=case["scale"], budget=budget)
+    say(f"stream_cqs auto: N={info['n_blocks']} k={info['quorum_size']} {rep}")
+    assert info["n_blocks"] > 1 and rep["peak_device_bytes"] <= budget
+    o_r, l_r, rep_r = attn.stream_budgeted(qh, kh, vh, causal=True, scale=case["scale"], budget=budget)
+    assert max_abs_err(o.numpy(), o_r.numpy()) <= 5e-3 and lse_err(lse.numpy(), l_r.numpy()) <= 1e-3
+    assert rep["h2d_bytes"] > rep_r["h2d_bytes"]
+
+
+def test_stream_cqs_empty_keys_and_errors():
+    case = gen.prefill_inputs(1, 4, 2, 64, 64, 64, kind="bf16", seed=5)
+    qh, kh, vh = (_pinned(case[c]) for c in "qkv")
+    empty = torch.empty((1, 0, 2, 64), dtype=torch.bfloat16, pin_memory=True)
+    o, lse, info, _ = attn.stream_cqs(qh, empty, empty, causal=True, budget=1 << 30, n_blocks=7)
+    assert np.all(o.numpy() == 0) and np.all(np.isneginf(lse.numpy()))
+    with pytest.raises(attn.AttnError) as e:
+        attn.stream_cqs(qh, kh, vh, causal=True, budget=1 << 30, n_blocks=5)
+    assert e.value.status == 2
+    q_pageable = torch.from_numpy(case["q"].view(np.int16)).view(torch.bfloat16)
+    with pytest.raises(attn.AttnError) as e:
+        attn.stream_cqs(q_pageable, kh, vh, causal=True, budget=1 << 30)
+    assert e.value.status == 1
+    free0 = torch.cuda.mem_get_info()[0]
+    with pytest.raises(attn.AttnError) as e:
+        attn.stream_cqs(qh, kh, vh, causal=True, budget=4096)
+    assert e.value.status == 3 and torch.cuda.mem_get_info()[0] == free0

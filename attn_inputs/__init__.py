@@ -174,8 +174,9 @@ def page_table(lengths, page_size, spare, seed):
 
 
 def decode_inputs(B, Hq, Hkv, D, lengths, kv="bf16", page_size=512, paged=True, spare=8,
-                  seed=0x5EED, t_alloc=None):
-    """Decode operands: q [B,Hq,D] bf16 and a KV cache.
+                  seed=0x5EED, t_alloc=None, n_q=None):
+    """Decode operands: q [B,Hq,D] bf16 (or [B,n_q,Hq,D] for multi-token
+    decode when n_q is given) and a KV cache.
 
     paged:  caches [P, Hkv, page_size, D] addressed through a page table.
     contiguous: caches [B, Hkv, t_alloc, D] (t_alloc defaults to max length).
@@ -183,7 +184,7 @@ def decode_inputs(B, Hq, Hkv, D, lengths, kv="bf16", page_size=512, paged=True, 
         (scales [Hkv] for K and for V).
     Unused cache slots are poisoned so that any stray read is visible."""
     lengths = np.asarray(lengths, dtype=np.int32)
-    q = normal((B, Hq, D), seed, TID_Q, "bf16")
+    q = normal((B, Hq, D) if n_q is None else (B, n_q, Hq, D), seed, TID_Q, "bf16")
     maxlen = int(lengths.max()) if lengths.size else 0
     if paged:
         table, P = page_table(lengths, page_size, spare, seed)
@@ -202,7 +203,7 @@ def decode_inputs(B, Hq, Hkv, D, lengths, kv="bf16", page_size=512, paged=True, 
             p = int(table[b, j]) if paged else b
             n = min(page_size, L - j * page_size)
             valid[p, :n] = True
-    out = {"q": q, "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "lengths": lengths, "kv": kv,
+    out = {"q": q, "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "lengths": lengths, "kv": kv, "n_q": n_q,
            "page_table": table, "page_size": page_size, "num_pages": P, "max_pages": max_pages,
            "paged": paged, "scale": 1.0 / math.sqrt(D), "valid": valid}
     kf = normal(cache_shape, seed, TID_K, "f32")
@@ -251,6 +252,8 @@ WORKLOADS = {
     "llama13b_gqa_causal_bf16": dict(B=4, Hq=40, Hkv=8, S=4096, T=4096, D=128, kind="bf16", causal=True),
     "paged_splitkv_decode_bf16": dict(B=8, Hq=32, Hkv=8, D=128, lo=1024, hi=32768, page_size=512),
     "quant_decode": dict(B=4, Hq=32, Hkv=8, D=128, T=(4096, 65536)),
+    # speculative verification: the last n_q tokens of each sequence against a paged cache
+    "multi_token_decode": dict(B=8, Hq=32, Hkv=8, D=128, n_q=4, lo=1024, hi=32768, page_size=512),
     "stream_cqsa_causal_1m": dict(B=1, Hq=32, Hkv=8, S=1 << 20, T=1 << 20, D=128, kind="bf16",
                                   causal=True, budget=4_000_000_000),
 }

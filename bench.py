@@ -10,6 +10,8 @@ only unmasked (query, key) pairs at 4*D flop each.  Beside it, in the same run:
     timed launch streams from HBM rather than from the 256 MB last-level cache;
   * ``decode_quant``: the same decode over contiguous int8 and OCP e4m3fn
     caches (B=4, Hq=32, Hkv=8, D=128, T=65536) in GB/s of cache bytes;
+  * ``decode_multi``: multi-token decode (n_q=4 verified tokens per sequence)
+    over paged bf16 and int8 caches of the decode workload's shape, in GB/s;
   * ``roofline`` / ``decode.roofline``: achieved vs MI355X peak, timed with HIP
     events on the stream the kernels are launched on;
   * ``cpu_baseline``: the fp64 oracle on a bounded sample of query rows of the
@@ -233,6 +235,85 @@ def bench_decode_quant(args):
     return {"workload": "quant_decode", "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "T": T, "kv": res}
 
 
+def bench_decode_multi(args):
+    """Multi-token decode (B=8, Hq=32, Hkv=8, D=128, n_q=4 verified tokens per
+    sequence, 512-token pages, T_b ~ U[1024, 32768]) over bf16 and int8 paged
+    caches drawn on the device; GB/s counts each valid K/V byte (and int8
+    scale) once plus q/o/lse.  Beside it, single-token decode of the last
+    query token on the same cache."""
+    import numpy as np
+    import torch
+
+    import attn_inputs as gen
+    import exact_long_context_tiled_amd as attn
+
+    w = gen.WORKLOADS["multi_token_decode"]
+    B, Hq, Hkv, D, n_q, ps = w["B"], w["Hq"], w["Hkv"], w["D"], w["n_q"], w["page_size"]
+    seed = 0x5EED + 6
+    lens = gen.ragged_lengths(B, w["lo"], w["hi"], seed)
+    table, P = gen.page_table(lens, ps, 8, seed)
+    pt = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int32)).cuda()
+    lens_d = torch.from_numpy(lens.astype(np.int32)).cuda()
+    maxlen = int(lens.max())
+    valid = int(lens.sum())
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    q = torch.randn((B, n_q, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    q1 = q[:, -1].contiguous()
+    ws = torch.empty(attn.decode_multi_workspace_size(B, n_q, Hq, Hkv, D, maxlen), dtype=torch.uint8,
+                     device="cuda")
+    ws1 = torch.empty(attn.decode_workspace_size(B, Hq, Hkv, D, maxlen), dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, n_q, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, n_q), dtype=torch.float32, device="cuda")
+    o1 = torch.empty((B, Hq, D), dtype=torch.float32, device="cuda")
+    l1 = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    shape = (P, Hkv, ps, D)
+    res = {}
+    for kv in ("bf16", "int8"):
+        eb = 2 if kv == "bf16" else 1
+        cache_bytes = P * Hkv * ps * D * eb * 2
+        copies = max(2, math.ceil((1 << 30) / cache_bytes))
+        caches = []
+        for _ in range(copies):
+            if kv == "bf16":
+                k = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+                v = torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+                ks = vs = None
+            else:
+                k = torch.randint(-127, 128, shape, generator=g, dtype=torch.int8, device="cuda")
+                v = torch.randint(-127, 128, shape, generator=g, dtype=torch.int8, device="cuda")
+                ks = torch.rand((P, Hkv, ps), generator=g, device="cuda") * 0.02 + 0.005
+                vs = torch.rand((P, Hkv, ps), generator=g, device="cuda") * 0.02 + 0.005
+            caches.append((k, v, ks, vs))
+
+        def step(i, caches=caches, copies=copies):
+            k, v, ks, vs = caches[i % copies]
+            attn.decode_multi(q, k, v, lens_d, maxlen, page_table=pt, k_scale=ks, v_scale=vs, workspace=ws, out=o,
+                              lse=lse)
+
+        def step1(i, caches=caches, copies=copies):
+            k, v, ks, vs = caches[i % copies]
+            attn.decode_splitkv(q1, k, v, lens_d, maxlen, page_table=pt, k_scale=ks, v_scale=vs, workspace=ws1,
+                                out=o1, lse=l1)
+
+        steps = max(args.steps, copies * 4)
+        ms = timed(step, steps, max(args.warmup, copies), stream)
+        ms1 = timed(step1, steps, max(args.warmup, copies), stream)
+        kv_bytes = valid * Hkv * D * eb * 2 + (valid * Hkv * 4 * 2 if kv == "int8" else 0)
+        nbytes = kv_bytes + B * n_q * Hq * (D * (2 + 4) + 4)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"decode multi-token {kv} n_q={n_q}: {ms * 1e3:.2f} us/call, {gbs:.1f} GB/s "
+            f"(single-token on the same cache: {ms1 * 1e3:.2f} us)")
+        res[kv] = {"value": round(gbs, 2), "unit": "GB/s", "us_per_call": round(ms * 1e3, 3), "bytes": nbytes,
+                   "single_token_us_per_call": round(ms1 * 1e3, 3), "cache_copies": copies, "steps": steps,
+                   "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+        del caches
+    return {"workload": "multi_token_decode", "B": B, "n_q": n_q, "Hq": Hq, "Hkv": Hkv, "D": D,
+            "page_size": ps, "lengths": lens.tolist(), "kv": res}
+
+
 def cpu_baseline(case, w, target_s):
     import oracle
     import attn_inputs as gen
@@ -348,6 +429,7 @@ def main():
     if not args.no_decode:
         out["decode"] = bench_decode(args)
         out["decode_quant"] = bench_decode_quant(args)
+        out["decode_multi"] = bench_decode_multi(args)
     if args.stream or args.stream_cqs:
         out["stream"] = bench_stream(args)
     if args.calibrate_copy:

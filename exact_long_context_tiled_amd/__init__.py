@@ -14,6 +14,8 @@ from ._binding import (  # noqa: F401
     ATTN_FP8_E4M3,
     ATTN_INT8,
     AttnError,
+    decode_multi,
+    decode_multi_workspace_size,
     decode_splitkv,
     decode_workspace_size,
     last_error,
@@ -28,6 +30,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "AttnError", "prefill", "decode_splitkv", "decode_workspace_size", "merge_partials", "stream_budgeted",
+    "AttnError", "prefill", "decode_splitkv", "decode_workspace_size", "decode_multi",
+    "decode_multi_workspace_size", "merge_partials", "stream_budgeted",
     "stream_plan", "stream_cqs", "stream_cqs_plan", "last_error", "lib", "lib_path",
 ]

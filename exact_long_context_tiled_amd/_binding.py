@@ -59,6 +59,10 @@ def lib():
         L.attn_decode_workspace_size.restype = SZ
         L.attn_decode_splitkv.argtypes = [I, P, P, P, P, P, P, I, I, I, P, I, I, I, I, I, F, I, P, SZ, P, P, P]
         L.attn_decode_splitkv.restype = I
+        L.attn_decode_multi_workspace_size.argtypes = [I, I, I, I, I, I, I]
+        L.attn_decode_multi_workspace_size.restype = SZ
+        L.attn_decode_multi.argtypes = [I, P, P, P, P, P, P, I, I, I, P, I, I, I, I, I, I, F, I, P, SZ, P, P, P]
+        L.attn_decode_multi.restype = I
         L.attn_merge_partials.argtypes = [I, P, P, I64, I, P, P, P]
         L.attn_merge_partials.restype = I
         L.attn_stream_budgeted.argtypes = [I, P, P, P, I, I, I, I64, I64, I, I, F, SZ, I64, I64, P, P,
@@ -130,6 +134,16 @@ def decode_workspace_size(B, Hq, Hkv, D, max_kv_len, num_splits=0) -> int:
     return int(lib().attn_decode_workspace_size(B, Hq, Hkv, D, max_kv_len, num_splits))
 
 
+def _cache_dtype(k_cache, kv_dtype):
+    if kv_dtype == "fp8" or k_cache.dtype == torch.float8_e4m3fn:
+        return ATTN_FP8_E4M3
+    if k_cache.dtype == torch.int8:
+        return ATTN_INT8
+    if k_cache.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise ValueError(f"unsupported cache dtype {k_cache.dtype}")
+
+
 def decode_splitkv(q, k_cache, v_cache, kv_lens, max_kv_len, *, page_table=None, k_scale=None, v_scale=None,
                    kv_dtype=None, scale=None, num_splits=0, workspace=None, out=None, lse=None, return_lse=True):
     """Split-KV decode.  q [B,Hq,D] bf16; caches [P,Hkv,page,D] (paged) or
@@ -137,14 +151,7 @@ def decode_splitkv(q, k_cache, v_cache, kv_lens, max_kv_len, *, page_table=None,
     with kv_dtype='fp8').  Returns (o [B,Hq,D] fp32, lse [B,Hq] or None)."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (kv_lens, "kv_lens")):
         _need(t, n)
-    if kv_dtype == "fp8" or k_cache.dtype == torch.float8_e4m3fn:
-        kdt = ATTN_FP8_E4M3
-    elif k_cache.dtype == torch.int8:
-        kdt = ATTN_INT8
-    elif k_cache.dtype == torch.bfloat16:
-        kdt = ATTN_BF16
-    else:
-        raise ValueError(f"unsupported cache dtype {k_cache.dtype}")
+    kdt = _cache_dtype(k_cache, kv_dtype)
     B, Hq, D = q.shape
     num_pages, Hkv, page_size = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
     max_pages = page_table.shape[1] if page_table is not None else 0
@@ -161,6 +168,37 @@ def decode_splitkv(q, k_cache, v_cache, kv_lens, max_kv_len, *, page_table=None,
                                      _ptr(page_table), max_pages, page_size, num_pages, _ptr(kv_lens), max_kv_len,
                                      B, Hq, Hkv, D, scale, num_splits, _ptr(workspace), workspace.numel(),
                                      _ptr(out), _ptr(lse), _stream()))
+    return out, lse
+
+
+def decode_multi_workspace_size(B, n_q, Hq, Hkv, D, max_kv_len, num_splits=0) -> int:
+    return int(lib().attn_decode_multi_workspace_size(B, n_q, Hq, Hkv, D, max_kv_len, num_splits))
+
+
+def decode_multi(q, k_cache, v_cache, kv_lens, max_kv_len, *, page_table=None, k_scale=None, v_scale=None,
+                 kv_dtype=None, scale=None, num_splits=0, workspace=None, out=None, lse=None, return_lse=True):
+    """Multi-token decode: q [B,n_q,Hq,D] bf16 = the last n_q tokens of each
+    sequence (causal among themselves); caches as decode_splitkv.
+    Returns (o [B,n_q,Hq,D] fp32, lse [B,Hq,n_q] or None)."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (kv_lens, "kv_lens")):
+        _need(t, n)
+    kdt = _cache_dtype(k_cache, kv_dtype)
+    B, n_q, Hq, D = q.shape
+    num_pages, Hkv, page_size = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    max_pages = page_table.shape[1] if page_table is not None else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = decode_multi_workspace_size(B, n_q, Hq, Hkv, D, max_kv_len, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, n_q, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, n_q), dtype=torch.float32, device=q.device)
+    _check(lib().attn_decode_multi(kdt, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale),
+                                   _ptr(page_table), max_pages, page_size, num_pages, _ptr(kv_lens), max_kv_len,
+                                   B, n_q, Hq, Hkv, D, scale, num_splits, _ptr(workspace), workspace.numel(),
+                                   _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 

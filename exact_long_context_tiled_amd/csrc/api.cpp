@@ -90,22 +90,28 @@ extern "C" attn_status attn_prefill(attn_dtype dt, const void* q, const void* k,
                          : launch_prefill_f32(a, D, (hipStream_t)stream);
 }
 
-extern "C" size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len, int num_splits) {
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || max_kv_len < 0 || num_splits < 0 || Hq % Hkv) return 0;
-  return decode_workspace_bytes(B, Hkv, Hq / Hkv, D, num_splits > 0 ? num_splits : kDecodeMaxAutoUnits);
+namespace {
+
+constexpr int kDecodeMaxQueryTokens = 64;
+
+size_t decode_ws(int B, int Hq, int Hkv, int D, int n_q, int max_kv_len, int num_splits) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || n_q <= 0 || max_kv_len < 0 || num_splits < 0 || Hq % Hkv) return 0;
+  return decode_workspace_bytes(B, Hkv, n_q * (Hq / Hkv), D, num_splits > 0 ? num_splits : kDecodeMaxAutoUnits);
 }
 
-extern "C" attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, const void* k_cache,
-                                           const void* v_cache, const float* k_scale, const float* v_scale,
-                                           const int32_t* page_table, int max_pages, int page_size, int num_pages,
-                                           const int32_t* kv_lens, int max_kv_len, int B, int Hq, int Hkv, int D,
-                                           float scale, int num_splits, void* workspace, size_t workspace_bytes,
-                                           float* o, float* lse, void* stream) {
+attn_status decode_impl(attn_dtype kv_dt, const void* q, const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale, const int32_t* page_table, int max_pages,
+                        int page_size, int num_pages, const int32_t* kv_lens, int max_kv_len, int B, int n_q, int Hq,
+                        int Hkv, int D, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                        float* o, float* lse, void* stream) {
   if (kv_dt != ATTN_BF16 && kv_dt != ATTN_INT8 && kv_dt != ATTN_FP8_E4M3)
     return set_error(ATTN_E_UNSUPPORTED, "decode: KV dtype must be bf16, int8 or fp8 e4m3 (got %d)", (int)kv_dt);
   if (D != 64 && D != 128) return set_error(ATTN_E_UNSUPPORTED, "decode: D must be 64 or 128 (got %d)", D);
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || max_kv_len < 0 || num_splits < 0)
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || max_kv_len < 0 || num_splits < 0 || n_q <= 0)
     return set_error(ATTN_E_INVALID, "decode: invalid sizes");
+  if (n_q > kDecodeMaxQueryTokens)
+    return set_error(ATTN_E_UNSUPPORTED, "decode: at most %d query tokens per sequence (got %d)",
+                     kDecodeMaxQueryTokens, n_q);
   if (Hq % Hkv) return set_error(ATTN_E_INVALID, "decode: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   const int G = Hq / Hkv;
   if (G > 8) return set_error(ATTN_E_UNSUPPORTED, "decode: at most 8 query heads per KV head (got %d)", G);
@@ -134,7 +140,7 @@ extern "C" attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, cons
   const double groups = (double)B * Hkv * ((max_kv_len + kDecodeGroup - 1) / kDecodeGroup);
   if (groups * (num_splits > 0 ? num_splits : kDecodeMaxAutoUnits) > 4e18)
     return set_error(ATTN_E_UNSUPPORTED, "decode: batch too large");
-  const size_t need = decode_workspace_bytes(B, Hkv, G, D, num_splits > 0 ? num_splits : kDecodeMaxAutoUnits);
+  const size_t need = decode_ws(B, Hq, Hkv, D, n_q, max_kv_len, num_splits);
   if (!workspace || workspace_bytes < need)
     return set_error(ATTN_E_INVALID, "decode: workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
   if (((uintptr_t)workspace) & 255) return set_error(ATTN_E_INVALID, "decode: workspace must be 256-byte aligned");
@@ -153,17 +159,51 @@ extern "C" attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, cons
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
+  a.n_q = n_q;
   a.n_units = num_splits;
   a.scale_log2 = scale * kLog2e;
   const size_t segs = (size_t)B * Hkv;
   const size_t rec_bytes =
-      ((size_t)((num_splits > 0 ? num_splits : kDecodeMaxAutoUnits) + segs) * decode_record_floats(G, D) *
+      ((size_t)((num_splits > 0 ? num_splits : kDecodeMaxAutoUnits) + segs) * decode_record_floats(n_q * G, D) *
            sizeof(float) + 255) / 256 * 256;
   a.part = (float*)workspace;
   a.seg_info = (int32_t*)((char*)workspace + rec_bytes);
   a.o = o;
   a.lse = lse;
   return launch_decode(kv_dt, a, D, G, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len, int num_splits) {
+  return decode_ws(B, Hq, Hkv, D, 1, max_kv_len, num_splits);
+}
+
+extern "C" attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, const void* k_cache,
+                                           const void* v_cache, const float* k_scale, const float* v_scale,
+                                           const int32_t* page_table, int max_pages, int page_size, int num_pages,
+                                           const int32_t* kv_lens, int max_kv_len, int B, int Hq, int Hkv, int D,
+                                           float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                                           float* o, float* lse, void* stream) {
+  return decode_impl(kv_dt, q, k_cache, v_cache, k_scale, v_scale, page_table, max_pages, page_size, num_pages,
+                     kv_lens, max_kv_len, B, 1, Hq, Hkv, D, scale, num_splits, workspace, workspace_bytes, o, lse,
+                     stream);
+}
+
+extern "C" size_t attn_decode_multi_workspace_size(int B, int n_q, int Hq, int Hkv, int D, int max_kv_len,
+                                                   int num_splits) {
+  return decode_ws(B, Hq, Hkv, D, n_q, max_kv_len, num_splits);
+}
+
+extern "C" attn_status attn_decode_multi(attn_dtype kv_dt, const void* q, const void* k_cache, const void* v_cache,
+                                         const float* k_scale, const float* v_scale, const int32_t* page_table,
+                                         int max_pages, int page_size, int num_pages, const int32_t* kv_lens,
+                                         int max_kv_len, int B, int n_q, int Hq, int Hkv, int D, float scale,
+                                         int num_splits, void* workspace, size_t workspace_bytes, float* o,
+                                         float* lse, void* stream) {
+  return decode_impl(kv_dt, q, k_cache, v_cache, k_scale, v_scale, page_table, max_pages, page_size, num_pages,
+                     kv_lens, max_kv_len, B, n_q, Hq, Hkv, D, scale, num_splits, workspace, workspace_bytes, o, lse,
+                     stream);
 }
 
 extern "C" attn_status attn_merge_partials(int n, const float* o_parts, const float* lse_parts, int64_t R, int D,

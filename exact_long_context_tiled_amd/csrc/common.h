@@ -74,20 +74,23 @@ struct DecodeArgs {
   const int32_t* kv_lens;
   int max_kv_len;  // lengths are clamped to [0, max_kv_len]
   int B, Hq, Hkv;
+  int n_q;      // query tokens per sequence (rows of the segment: n_q * G)
   int n_units;  // N
   float scale_log2;
-  float* part;       // records [N + B*Hkv - 1][G*D + 16]: O rows, then lse (log2) padded to 16
+  float* part;       // records [N + B*Hkv - 1][R*D + pad16(R)], R = n_q*G: O rows, then lse (log2)
   int32_t* seg_info; // [B*Hkv][2]: first record, record count (written by the segment's first unit)
-  float* o;          // [B, Hq, D]
-  float* lse;        // [B, Hq] or null
+  float* o;          // [B, n_q, Hq, D]
+  float* lse;        // [B, Hq, n_q] or null
 };
 
 constexpr int kDecodeGroup = 16;          // tokens per group (>= tokens per wave load step)
 constexpr int kDecodeMaxAutoUnits = 2048; // upper bound of the automatic unit count
 constexpr int kDecodeMaxUnits = 65535;
 
-int decode_record_floats(int G, int D);
-size_t decode_workspace_bytes(int B, int Hkv, int G, int D, int n_units_bound);
+// Floats of one partial record of `rows` query rows: O rows, then the rows' lse
+// padded to a multiple of 16.
+__host__ __device__ inline int decode_record_floats(int rows, int D) { return rows * D + (rows + 15) / 16 * 16; }
+size_t decode_workspace_bytes(int B, int Hkv, int rows, int D, int n_units_bound);
 // n_units == 0 picks one work-group per compute unit (at most
 // kDecodeMaxAutoUnits); the merge kernel runs after the split kernel.
 attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a, int D, int G, hipStream_t stream);

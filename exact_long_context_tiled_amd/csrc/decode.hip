@@ -214,7 +214,11 @@ __device__ void group_prefix(const int32_t* __restrict__ lens, int B, int max_le
 constexpr int kDecodeWaves = 4;  // waves per work-group
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 
-template <int KV, int D, int G>
+// Rows of a segment: R = n_q * G query rows (query token s, head g) share the
+// (sequence, KV head) KV.  They are processed TQ query tokens (TQ * G <= 8
+// rows, what the registers hold) at a time; a piece's later row chunks re-read
+// the piece's K/V right after the first, from the caches.
+template <int KV, int D, int G, int TQ>
 __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs a) {
   constexpr int EB = KvTraits<KV>::kBytes;
   constexpr int EPL = 16 / EB;   // elements per lane slice
@@ -222,11 +226,13 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
   constexpr int TPW = 64 / LPT;  // tokens per wave per load step (token slots)
   constexpr int U = 4;           // load steps per iteration
   constexpr int TPI = TPW * U;   // tokens per wave per iteration
-  constexpr int REC = G * D + 16;
+  constexpr int RC = TQ * G;      // rows per chunk
+  const int RT = a.n_q * G;      // rows per segment
+  const int REC = decode_record_floats(RT, D);
   static_assert(kDecodeGroup % TPW == 0, "a load step must not straddle a group");
   extern __shared__ int64_t pre[];  // [B + 1]
-  __shared__ float red_acc[kDecodeWaves][G * D];
-  __shared__ float red_m[kDecodeWaves][G], red_l[kDecodeWaves][G];
+  __shared__ float red_acc[kDecodeWaves][RC * D];
+  __shared__ float red_m[kDecodeWaves][RC], red_l[kDecodeWaves][RC];
   __shared__ int64_t wsum[kDecodeWaves];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -266,15 +272,27 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
     const int t1 = __builtin_amdgcn_readfirstlane(min(T, (j0 + (int)(pend - pos)) * kDecodeGroup));
     const int seg = b * a.Hkv + hk;
     const bool whole = j0 == 0 && pend == seg_end;
-    const int64_t row0 = (int64_t)b * a.Hq + (int64_t)hk * G;  // first (b, h) row of this group
-
-    // query slices as exact bf16 pairs for the packed dot product; the score
-    // multiplier carries scale*log2(e) (and the e4m3 per-head K scale)
-    bf16x2 q2[G][EPL / 2];
-    float smul = a.scale_log2;
+    const int n_q = a.n_q;
+    float smul = a.scale_log2;  // scale*log2(e) (and the e4m3 per-head K scale)
     if constexpr (KV == ATTN_FP8_E4M3) smul *= a.k_scale[hk];
-    {
-      const uint16_t* qb = (const uint16_t*)a.q + row0 * D + part * EPL;
+    const int64_t hk_rows = (int64_t)hk * a.page_size;
+    float* rec = a.part + (int64_t)(unit + seg) * REC;
+    for (int s0 = 0; s0 < n_q; s0 += TQ) {
+    // query token s sits at position T - n_q + s and sees the keys before
+    // T - (n_q - 1 - s); rows past the last query token repeat it (not written)
+    const int tq_n = min(TQ, n_q - s0);
+    int lim[TQ];
+#pragma unroll
+    for (int j = 0; j < TQ; ++j) lim[j] = max(t0, min(t1, T - (n_q - 1 - (s0 + min(j, tq_n - 1)))));
+    const int tend = lim[TQ - 1];  // this chunk reads keys [t0, tend)
+
+    // query slices as exact bf16 pairs for the packed dot product
+    bf16x2 q2[RC][EPL / 2];
+#pragma unroll
+    for (int j = 0; j < TQ; ++j) {
+      // q row (b, s, hk*G + g) of [B, n_q, Hq, D]
+      const uint16_t* qb = (const uint16_t*)a.q +
+                           (((int64_t)b * n_q + s0 + min(j, tq_n - 1)) * a.Hq + (int64_t)hk * G) * D + part * EPL;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
 #pragma unroll
@@ -282,20 +300,19 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
           const uint4 raw = *(const uint4*)(qb + (int64_t)g * D + e);
           const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) q2[g][e / 2 + i] = __builtin_bit_cast(bf16x2, wd[i]);
+          for (int i = 0; i < 4; ++i) q2[j * G + g][e / 2 + i] = __builtin_bit_cast(bf16x2, wd[i]);
         }
       }
     }
 
-    float m[G], l[G], acc[G][EPL];
+    float m[RC], l[RC], acc[RC][EPL];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int g = 0; g < RC; ++g) {
       m[g] = -INFINITY;
       l[g] = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc[g][e] = 0.f;
     }
-    const int64_t hk_rows = (int64_t)hk * a.page_size;
 
     // Loads of one iteration (U steps of TPW tokens).  TPW consecutive tokens
     // from a TPW-aligned index never straddle a page and every step index is
@@ -314,7 +331,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
       for (int u = 0; u < U; ++u) {
         // first token of the step, wave-uniform and inside the piece;
         // readfirstlane keeps it (and the page-table read) on the scalar unit
-        const int tc = __builtin_amdgcn_readfirstlane(min(g0 + u * TPW, t1 - 1));
+        const int tc = __builtin_amdgcn_readfirstlane(min(g0 + u * TPW, tend - 1));
         if (a.page_table) {
           // read through the constant address space: a scalar (SMEM) load
           const auto* pt = (const __attribute__((address_space(4))) int32_t*)a.page_table;
@@ -329,7 +346,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
       // keep the other buffer's loads in flight)
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int64_t row = step_row[u] + min(g0 + u * TPW + slot, t1 - 1);
+        const int64_t row = step_row[u] + min(g0 + u * TPW + slot, tend - 1);
         bf.kr[u] = *(const uint4*)(kb + row * (D * EB) + lane_off);
         bf.vr[u] = *(const uint4*)(vb + row * (D * EB) + lane_off);
         if constexpr (KV == ATTN_INT8) {
@@ -342,30 +359,30 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
     };
     auto consume = [&](int g0, const Buf& bf) {
       // raw scores of the U tokens of this lane's slot (int8: times the token's K scale)
-      float s[U][G];
+      float s[U][RC];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         bf16x2 kp[EPL / 2];
         k_pairs<KV>(bf.kr[u], kp);
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
+        for (int g = 0; g < RC; ++g) {
           float d = 0.f;
 #pragma unroll
           for (int i = 0; i < EPL / 2; ++i) d = __builtin_amdgcn_fdot2_f32_bf16(q2[g][i], kp[i], d, false);
           s[u][g] = d;
         }
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
+        for (int g = 0; g < RC; ++g) {
           s[u][g] = token_sum<LPT>(s[u][g]);
           if constexpr (KV == ATTN_INT8) s[u][g] *= bf.ksc[u];
         }
       }
-      if (g0 + TPI > t1) {  // the piece's last iteration: tokens past its end weigh nothing
+      if (g0 + TPI > lim[0]) {  // near the end: keys past a row's limit weigh nothing
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-          const bool ok = g0 + u * TPW + slot < t1;
+          const int tok = g0 + u * TPW + slot;
 #pragma unroll
-          for (int g = 0; g < G; ++g) s[u][g] = ok ? s[u][g] : -INFINITY;
+          for (int g = 0; g < RC; ++g) s[u][g] = tok < lim[g / G] ? s[u][g] : -INFINITY;
         }
       }
       float vv[U][EPL];
@@ -376,10 +393,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
       // than 8, so p <= 256 and the rescale of the accumulators is skipped
       // for the whole wave on most iterations; any reference gives the exact
       // result.
-      float tx[G];
+      float tx[RC];
       bool grow = false;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
+      for (int g = 0; g < RC; ++g) {
         float mx = s[0][g];
 #pragma unroll
         for (int u = 1; u < U; ++u) mx = fmaxf(mx, s[u][g]);
@@ -388,7 +405,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
       }
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
+        for (int g = 0; g < RC; ++g) {
           const float m_new = fmaxf(m[g], tx[g]);
           const float alpha = __builtin_amdgcn_exp2f(m[g] - (m_new == -INFINITY ? 0.f : m_new));
           m[g] = m_new;
@@ -398,7 +415,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
         }
       }
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
+      for (int g = 0; g < RC; ++g) {
         const float nm = m[g] == -INFINITY ? 0.f : -m[g];
         float p[U];
 #pragma unroll
@@ -427,7 +444,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
     // them.)
     Buf b0, b1;
     int g0 = t0 + wu * TPI;
-    const int n_it = g0 < t1 ? (t1 - g0 + kStride - 1) / kStride : 0;  // iterations of this wave
+    const int n_it = g0 < tend ? (tend - g0 + kStride - 1) / kStride : 0;  // iterations of this wave
     if (n_it > 0) {
       issue(g0, b0);
       int k = 0;
@@ -444,14 +461,14 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
     }
 
     // combine the token slots of the wave (lanes LPT, 2*LPT, ... apart hold the same d slice)
-    if constexpr (LPT <= 4) combine_lanes<4, G, EPL>(m, l, acc);
-    if constexpr (LPT <= 8) combine_lanes<8, G, EPL>(m, l, acc);
-    if constexpr (LPT <= 16) combine_lanes<16, G, EPL>(m, l, acc);
-    combine_lanes<32, G, EPL>(m, l, acc);
+    if constexpr (LPT <= 4) combine_lanes<4, RC, EPL>(m, l, acc);
+    if constexpr (LPT <= 8) combine_lanes<8, RC, EPL>(m, l, acc);
+    if constexpr (LPT <= 16) combine_lanes<16, RC, EPL>(m, l, acc);
+    combine_lanes<32, RC, EPL>(m, l, acc);
     // combine the waves through LDS
     if (slot == 0) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
+      for (int g = 0; g < RC; ++g) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) red_acc[w][g * D + part * EPL + e] = acc[g][e];
         if (part == 0) {
@@ -463,9 +480,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
     __syncthreads();
     float vmul = 1.f;
     if constexpr (KV == ATTN_FP8_E4M3) vmul = a.v_scale[hk];
-    // a piece always holds a key, so every denominator below is positive
-    float* rec = a.part + (int64_t)(unit + seg) * REC;
-    for (int idx = tid; idx < G * D; idx += kDecodeThreads) {
+    // rows s0*G .. s0*G + RC - 1 of the segment's record; a row whose keys all
+    // lie past its limit has a zero sum: O = 0, lse = -inf
+    const int n_rows = tq_n * G;
+    for (int idx = tid; idx < n_rows * D; idx += kDecodeThreads) {
       const int g = idx / D;
       float M = red_m[0][g];
 #pragma unroll
@@ -477,25 +495,31 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
         num = fmaf(f, red_acc[ww][idx], num);
         den = fmaf(f, red_l[ww][g], den);
       }
-      const float val = num * (vmul / den);
-      if (whole) a.o[row0 * D + idx] = val;  // rows row0 .. row0+G-1 are consecutive
-      else rec[idx] = val;
-    }
-    if (tid < 16) {  // the piece's lse (log2), padded to a whole 64-byte line
-      float v = 0.f;
-      if (tid < G) {
-        float M = red_m[0][tid];
-#pragma unroll
-        for (int ww = 1; ww < kDecodeWaves; ++ww) M = fmaxf(M, red_m[ww][tid]);
-        float den = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < kDecodeWaves; ++ww)
-          den = fmaf(red_m[ww][tid] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[ww][tid] - M), red_l[ww][tid], den);
-        v = M + __log2f(den);
+      const float val = den > 0.f ? num * (vmul / den) : 0.f;
+      if (whole) {  // o row (b, s0 + g / G, hk*G + g % G) of [B, n_q, Hq, D]
+        const int64_t orow = ((int64_t)b * n_q + s0 + g / G) * a.Hq + (int64_t)hk * G + g % G;
+        a.o[orow * D + idx % D] = val;
+      } else {
+        rec[(int64_t)s0 * G * D + idx] = val;
       }
-      if (!whole) rec[G * D + tid] = v;
-      else if (tid < G && a.lse) a.lse[row0 + tid] = v * kLn2;
     }
+    if (tid < n_rows) {  // the piece's lse (log2) of each row
+      float M = red_m[0][tid];
+#pragma unroll
+      for (int ww = 1; ww < kDecodeWaves; ++ww) M = fmaxf(M, red_m[ww][tid]);
+      float den = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < kDecodeWaves; ++ww)
+        den = fmaf(red_m[ww][tid] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[ww][tid] - M), red_l[ww][tid], den);
+      const float v = den > 0.f ? M + __log2f(den) : -INFINITY;
+      if (!whole) {
+        rec[(int64_t)RT * D + s0 * G + tid] = v;
+      } else if (a.lse) {  // lse [B, Hq, n_q]
+        a.lse[((int64_t)b * a.Hq + (int64_t)hk * G + tid % G) * n_q + s0 + tid / G] = v * kLn2;
+      }
+    }
+    __syncthreads();  // LDS is reused by the next row chunk
+    }  // row chunks
     if (tid == 0 && j0 == 0) {
       // records of this segment: units unit .. (the unit holding its last group)
       const int last = whole ? unit : (int)((seg_end * N - 1) / W);
@@ -503,21 +527,24 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
       a.seg_info[2 * seg + 1] = last - unit + 1;
     }
     pos = pend;
-    __syncthreads();  // LDS is reused by the next piece
   }
 }
 
-// One wave per output row (b, h): merges the records of its segment by
+// One wave per output row (b, s, h): merges the records of its segment by
 // log-sum-exp, or writes O = 0, lse = -inf for an empty sequence.  Segments
 // finished by a single unit were written by the split kernel already.
 template <int D>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a, int G) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= (int64_t)a.B * a.Hq) return;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // o row of [B, n_q, Hq, D]
+  const int n_q = a.n_q;
+  if (row >= (int64_t)a.B * n_q * a.Hq) return;
   const int lane = threadIdx.x & 63;
-  const int b = (int)(row / a.Hq), h = (int)(row - (int64_t)b * a.Hq);
+  const int h = (int)(row % a.Hq);
+  const int64_t bs = row / a.Hq;
+  const int b = (int)(bs / n_q), sq = (int)(bs - (int64_t)b * n_q);
   const int hk = h / G, g = h - hk * G;
   const int seg = b * a.Hkv + hk;
+  const int64_t lrow = ((int64_t)b * a.Hq + h) * n_q + sq;  // lse [B, Hq, n_q]
   // both loads in flight together; seg_info is only meaningful for a non-empty sequence
   const int T = clamp_len(a.kv_lens[b], a.max_kv_len);
   const int first = a.seg_info[2 * seg], n = a.seg_info[2 * seg + 1];
@@ -526,25 +553,28 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a, int G) 
   if (T == 0) {
 #pragma unroll
     for (int k = 0; k < CPL; ++k) orow[lane + 64 * k] = 0.f;
-    if (lane == 0 && a.lse) a.lse[row] = -INFINITY;
+    if (lane == 0 && a.lse) a.lse[lrow] = -INFINITY;
     return;
   }
   if (n <= 1) return;
-  const int REC = G * D + 16;
+  const int RT = n_q * G;
+  const int REC = decode_record_floats(RT, D);
+  const int r_rec = sq * G + g;  // the row's place in a record
   const float* rec0 = a.part + (int64_t)first * REC;
   float mx = -INFINITY, den = 0.f, acc[CPL];
 #pragma unroll
   for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
   // eight records at a time, all their loads issued before the first use;
-  // an online log-sum-exp update folds each batch in
+  // an online log-sum-exp update folds each batch in.  A record of a row
+  // that saw no key there has lse = -inf and weight 0.
   for (int c0 = 0; c0 < n; c0 += 8) {
     float lv[8], x[8][CPL];
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const float* rec = rec0 + (int64_t)min(c0 + r, n - 1) * REC;  // past the end: a valid record, weighted 0
-      lv[r] = rec[G * D + g];
+      lv[r] = rec[(int64_t)RT * D + r_rec];
 #pragma unroll
-      for (int k = 0; k < CPL; ++k) x[r][k] = rec[g * D + lane + 64 * k];
+      for (int k = 0; k < CPL; ++k) x[r][k] = rec[(int64_t)r_rec * D + lane + 64 * k];
     }
     float bm = -INFINITY;
 #pragma unroll
@@ -552,7 +582,8 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a, int G) 
       if (c0 + r >= n) lv[r] = -INFINITY;
       bm = fmaxf(bm, lv[r]);
     }
-    const float M = fmaxf(mx, bm);  // finite: every record holds a key
+    const float M = fmaxf(mx, bm);
+    if (M == -INFINITY) continue;  // nothing seen yet
     const float f = __builtin_amdgcn_exp2f(mx - M);
     den *= f;
 #pragma unroll
@@ -566,16 +597,16 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a, int G) 
     }
     mx = M;
   }
-  const float inv = 1.f / den;
+  const float inv = den > 0.f ? 1.f / den : 0.f;
 #pragma unroll
   for (int k = 0; k < CPL; ++k) orow[lane + 64 * k] = acc[k] * inv;
-  if (lane == 0 && a.lse) a.lse[row] = (mx + __log2f(den)) * kLn2;
+  if (lane == 0 && a.lse) a.lse[lrow] = den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
 }
 
-template <int KV, int D, int G>
+template <int KV, int D, int G, int TQ>
 attn_status launch_one(DecodeArgs a, hipStream_t stream) {
   const size_t lds = (size_t)(a.B + 1) * sizeof(int64_t);
-  auto kern = decode_split_kernel<KV, D, G>;
+  auto kern = decode_split_kernel<KV, D, G, TQ>;
   static bool lds_set = false;  // the length prefix may take the LDS past the default dynamic limit
   if (!lds_set) {
     if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -593,22 +624,39 @@ attn_status launch_one(DecodeArgs a, hipStream_t stream) {
   hipLaunchKernelGGL(kern, dim3(a.n_units), dim3(kDecodeThreads), lds, stream, a);
   attn_status st = check_launch("decode_split");
   if (st != ATTN_OK) return st;
-  const int64_t rows = (int64_t)a.B * a.Hq;
+  const int64_t rows = (int64_t)a.B * a.n_q * a.Hq;
   hipLaunchKernelGGL(decode_merge_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a, G);
   return check_launch("decode_merge");
+}
+
+// Query tokens per row chunk: enough to cover n_q in as few chunks as the
+// registers allow (TQ * G <= 8).
+template <int KV, int D, int G>
+attn_status launch_tq(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int kMaxTq = 8 / G;
+  const int want = std::min(a.n_q, kMaxTq);
+  if (want <= 1) return launch_one<KV, D, G, 1>(a, stream);
+  if constexpr (kMaxTq >= 2) {
+    if (want <= 2) return launch_one<KV, D, G, 2>(a, stream);
+  }
+  if constexpr (kMaxTq >= 4) {
+    if (want <= 4) return launch_one<KV, D, G, 4>(a, stream);
+  }
+  if constexpr (kMaxTq >= 8) return launch_one<KV, D, G, 8>(a, stream);
+  return set_error(ATTN_E_DEVICE, "decode: no row-chunk variant");
 }
 
 template <int KV, int D>
 attn_status launch_g(const DecodeArgs& a, int G, hipStream_t stream) {
   switch (G) {
-    case 1: return launch_one<KV, D, 1>(a, stream);
-    case 2: return launch_one<KV, D, 2>(a, stream);
-    case 3: return launch_one<KV, D, 3>(a, stream);
-    case 4: return launch_one<KV, D, 4>(a, stream);
-    case 5: return launch_one<KV, D, 5>(a, stream);
-    case 6: return launch_one<KV, D, 6>(a, stream);
-    case 7: return launch_one<KV, D, 7>(a, stream);
-    case 8: return launch_one<KV, D, 8>(a, stream);
+    case 1: return launch_tq<KV, D, 1>(a, stream);
+    case 2: return launch_tq<KV, D, 2>(a, stream);
+    case 3: return launch_tq<KV, D, 3>(a, stream);
+    case 4: return launch_tq<KV, D, 4>(a, stream);
+    case 5: return launch_tq<KV, D, 5>(a, stream);
+    case 6: return launch_tq<KV, D, 6>(a, stream);
+    case 7: return launch_tq<KV, D, 7>(a, stream);
+    case 8: return launch_tq<KV, D, 8>(a, stream);
   }
   return set_error(ATTN_E_UNSUPPORTED, "decode: query heads per KV head must be 1..8 (got %d)", G);
 }
@@ -620,12 +668,10 @@ attn_status launch_d(const DecodeArgs& a, int D, int G, hipStream_t stream) {
 
 }  // namespace
 
-int decode_record_floats(int G, int D) { return G * D + 16; }
-
-size_t decode_workspace_bytes(int B, int Hkv, int G, int D, int n_units_bound) {
+size_t decode_workspace_bytes(int B, int Hkv, int rows, int D, int n_units_bound) {
   const size_t segs = (size_t)B * (size_t)Hkv;
   const size_t recs = (size_t)n_units_bound + segs;  // record indices stay below N + segments - 1
-  const size_t rec_bytes = (recs * (size_t)decode_record_floats(G, D) * sizeof(float) + 255) / 256 * 256;
+  const size_t rec_bytes = (recs * (size_t)decode_record_floats(rows, D) * sizeof(float) + 255) / 256 * 256;
   return rec_bytes + (segs * 2 * sizeof(int32_t) + 255) / 256 * 256;
 }
 

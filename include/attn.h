@@ -127,6 +127,39 @@ attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, const void* k_c
                                 void* workspace, size_t workspace_bytes, float* o, float* lse, void* stream);
 
 /*
+ * Workspace bytes attn_decode_multi needs for these sizes (num_splits as
+ * passed to it; 0 = automatic).  Pure host arithmetic; 0 for invalid sizes.
+ */
+size_t attn_decode_multi_workspace_size(int B, int n_q, int Hq, int Hkv, int D, int max_kv_len, int num_splits);
+
+/*
+ * Multi-token decode (speculative verification): the last n_q tokens of each
+ * sequence query its KV cache at once.  Query token s of sequence b sits at
+ * absolute position kv_lens[b] - n_q + s (past length + local index: ONNX
+ * Runtime PR #33328 analysis, section 1) and sees keys j <= that position;
+ * the cache already holds the n_q new tokens.  The n_q * G query rows of a
+ * KV head share each K/V read of the split-KV scan (several queries per pass
+ * over the keys: ONNX Runtime PR #33328 analysis, section 2), in chunks of at
+ * most 8 rows; later chunks of a piece re-read its K/V from the caches.
+ * Everything else -- paging, int8 / e4m3 dequantisation, the balanced split
+ * and the log-sum-exp merge -- is as in attn_decode_splitkv.
+ *
+ *   q          device, [B, n_q, Hq, D] bf16
+ *   n_q        1..64 query tokens per sequence (n_q = 1 is attn_decode_splitkv)
+ *   workspace  >= attn_decode_multi_workspace_size(...) bytes, 256-byte aligned
+ *   o          device [B, n_q, Hq, D] fp32; lse device [B, Hq, n_q] fp32 or NULL
+ *   other arguments as attn_decode_splitkv.
+ * A row that sees no key (kv_lens[b] - n_q + s < 0) gets O = 0, lse = -inf.
+ * Errors: ATTN_E_INVALID, ATTN_E_UNSUPPORTED (D, kv_dt, G > 8, n_q > 64),
+ * ATTN_E_DEVICE.
+ */
+attn_status attn_decode_multi(attn_dtype kv_dt, const void* q, const void* k_cache, const void* v_cache,
+                              const float* k_scale, const float* v_scale, const int32_t* page_table, int max_pages,
+                              int page_size, int num_pages, const int32_t* kv_lens, int max_kv_len, int B, int n_q,
+                              int Hq, int Hkv, int D, float scale, int num_splits, void* workspace,
+                              size_t workspace_bytes, float* o, float* lse, void* stream);
+
+/*
  * Exact log-sum-exp merge of n partial results of the same R rows:
  *   M = max_c lse_c;  w_c = exp(lse_c - M);
  *   O = sum_c w_c O_c / sum_c w_c;  lse = M + log sum_c w_c.

@@ -105,13 +105,20 @@ def prefill(case, causal=True, rows=None):
 
 
 def decode(case):
-    """Oracle for a decode case built by attn_inputs.decode_inputs: (o [B,Hq,D], lse [B,Hq])."""
+    """Oracle for a decode case built by attn_inputs.decode_inputs: (o [B,Hq,D], lse [B,Hq]);
+    with n_q query tokens per sequence (the last n_q positions, causal among
+    themselves, bottom-right aligned to each sequence's length):
+    (o [B,n_q,Hq,D], lse [B,Hq,n_q])."""
     c = case
-    o, lse = attention(c["q"].reshape(c["B"], 1, c["Hq"], c["D"]), c["k"], c["v"], B=c["B"], Hq=c["Hq"],
-                       Hkv=c["Hkv"], S=1, T=0, D=c["D"], causal=False, scale=c["scale"], layout=1,
+    n_q = c.get("n_q")
+    S = 1 if n_q is None else n_q
+    o, lse = attention(c["q"].reshape(c["B"], S, c["Hq"], c["D"]), c["k"], c["v"], B=c["B"], Hq=c["Hq"],
+                       Hkv=c["Hkv"], S=S, T=0, D=c["D"], causal=n_q is not None, scale=c["scale"], layout=1,
                        k_scale=c.get("k_scale"), v_scale=c.get("v_scale"), page_table=c["page_table"],
                        page_size=c["page_size"], kv_lens=c["lengths"])
-    return o[:, 0], lse[:, :, 0]
+    if n_q is None:
+        return o[:, 0], lse[:, :, 0]
+    return o, lse
 
 
 def merge(o_parts, lse_parts):

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     syms = _declared_symbols()
     assert set(syms) >= {"attn_prefill", "attn_decode_splitkv", "attn_merge_partials", "attn_stream_budgeted",
                          "attn_stream_plan", "attn_decode_workspace_size", "attn_last_error", "attn_stream_cqs",
-                         "attn_stream_cqs_plan"}
+                         "attn_stream_cqs_plan", "attn_decode_multi", "attn_decode_multi_workspace_size"}
     for s in syms:
         assert hasattr(L, s), s
 
@@ -74,6 +74,17 @@ def test_decode_and_merge_validation():
     assert L.attn_merge_partials(2, None, None, 10, 64, None, None, None) == 1
     assert L.attn_merge_partials(2, None, None, 0, 64, None, None, None) == 0
     assert call(B=4096) == 2  # more sequences than the on-chip length prefix holds
+
+    def multi(n_q, **kw):
+        a = dict(args, **kw)
+        return L.attn_decode_multi(1, a["q"], a["k"], a["v"], a["ks"], a["vs"], a["pt"], a["maxp"], a["ps"],
+                                   a["npg"], a["lens"], a["maxlen"], a["B"], n_q, a["Hq"], a["Hkv"], a["D"],
+                                   a["scale"], a["ns"], a["ws"], a["wsb"], a["o"], a["lse"], a["st"])
+
+    assert multi(0) == 1 and multi(-1) == 1
+    assert multi(65) == 2  # more query tokens than supported
+    assert multi(4) == 1  # null pointers
+    assert multi(4, B=0) == 0
     assert call(ns=65536) == 2  # more work units than one grid dimension
     # workspace sizing is pure host arithmetic: one record of G*D outputs plus
     # a 16-float lse line per (work unit + segment), then two ints per segment
@@ -88,6 +99,14 @@ def test_decode_and_merge_validation():
         rnd((4 + 64) * (4 * 128 + 16) * 4) + rnd(64 * 8))
     assert attn.decode_workspace_size(3, 10, 2, 64, 100, num_splits=7) == (
         rnd((7 + 6) * (5 * 64 + 16) * 4) + rnd(6 * 8))
+    # multi-token: a record holds n_q * G rows, the lse line padded to 16 floats
+    assert attn.decode_multi_workspace_size(8, 4, 32, 8, 128, 32768, num_splits=4) == (
+        rnd((4 + 64) * (16 * 128 + 16) * 4) + rnd(64 * 8))
+    assert attn.decode_multi_workspace_size(3, 7, 10, 2, 64, 100, num_splits=7) == (
+        rnd((7 + 6) * (35 * 64 + 48) * 4) + rnd(6 * 8))
+    assert attn.decode_multi_workspace_size(8, 1, 32, 8, 128, 32768) == attn.decode_workspace_size(8, 32, 8, 128,
+                                                                                                   32768)
+    assert attn.decode_multi_workspace_size(8, 0, 32, 8, 128, 32768) == 0
 
 
 def _coverage(tasks, rep, S, T, causal, B):

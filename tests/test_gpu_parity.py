@@ -168,9 +168,9 @@ def gpu_decode(case, num_splits=0):
     pt = to_dev(case["page_table"]) if case["paged"] else None
     lens = to_dev(case["lengths"].astype(np.int32))
     maxlen = int(case["lengths"].max()) if len(case["lengths"]) else 0
-    o, lse = attn.decode_splitkv(q, k, v, lens, maxlen, page_table=pt, k_scale=ks, v_scale=vs,
-                                 kv_dtype="fp8" if kind == "fp8" else None, scale=case["scale"],
-                                 num_splits=num_splits)
+    fn = attn.decode_multi if case.get("n_q") is not None else attn.decode_splitkv
+    o, lse = fn(q, k, v, lens, maxlen, page_table=pt, k_scale=ks, v_scale=vs,
+                kv_dtype="fp8" if kind == "fp8" else None, scale=case["scale"], num_splits=num_splits)
     torch.cuda.synchronize()
     return o.cpu().numpy(), lse.cpu().numpy()
 
@@ -229,6 +229,53 @@ def test_decode_many_sequences_mixed_lengths():
         o, lse = gpu_decode(case, num_splits=ns)
         assert np.all(o[lens == 0] == 0) and np.all(np.isneginf(lse[lens == 0]))
         check_lp(o, lse, ro, rl, f"B=300 mixed lengths units={ns}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("G,n_q,D", [(4, 2, 128), (4, 4, 128), (1, 8, 128), (2, 3, 64), (5, 2, 128), (8, 3, 128),
+                                     (1, 13, 64)])
+def test_decode_multi_token_edge_cases(kv, G, n_q, D):
+    """Multi-token decode == oracle: lengths shorter than n_q (rows that see no
+    key), pieces ending inside the causal tail, 16-token pages and a
+    contiguous cache, over several work-unit counts."""
+    import oracle
+    Hkv = 2
+    lens = np.array([0, 1, 2, 3, 15, 16, 17, 100, 513, 2000], dtype=np.int32)
+    for paged in (True, False):
+        case = gen.decode_inputs(len(lens), G * Hkv, Hkv, D, lens, kv=kv, page_size=16, paged=paged, spare=3,
+                                 seed=300 + G * 10 + n_q, n_q=n_q)
+        ro, rl = oracle.decode(case)
+        for ns in (0, 1, 5, 1000):
+            say(f"multi-token {kv} G={G} n_q={n_q} D={D} paged={paged} units={ns}")
+            o, lse = gpu_decode(case, num_splits=ns)
+            assert o.shape == ro.shape and lse.shape == rl.shape
+            assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+            check_lp(o, lse, ro, rl, f"multi-token {kv} G={G} n_q={n_q} paged={paged} units={ns}")
+
+
+def test_decode_multi_one_token_is_splitkv():
+    """n_q = 1 through the multi-token entry point is the single-token call, bit for bit."""
+    lens = np.array([0, 7, 300, 4000], dtype=np.int32)
+    case = gen.decode_inputs(4, 32, 8, 128, lens, kv="int8", page_size=512, seed=31)
+    o1, l1 = gpu_decode(case)
+    case_m = dict(case, q=case["q"].reshape(4, 1, 32, 128), n_q=1)
+    om, lm = gpu_decode(case_m)
+    assert np.array_equal(om[:, 0], o1) and np.array_equal(lm[:, :, 0], l1, equal_nan=True)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+def test_decode_multi_token_full(kv):
+    """B=8 Hq=32 Hkv=8 D=128, n_q=4 verified tokens per sequence, paged 512-token cache,
+    T_b ~ U[1024, 32768]: every output vs the oracle."""
+    import oracle
+    w = gen.WORKLOADS["multi_token_decode"]
+    seed = 0x5EED + 6
+    lens = gen.ragged_lengths(w["B"], w["lo"], w["hi"], seed)
+    case = gen.decode_inputs(w["B"], w["Hq"], w["Hkv"], w["D"], lens, kv=kv, page_size=w["page_size"], seed=seed,
+                             n_q=w["n_q"])
+    o, lse = gpu_decode(case)
+    ro, rl = oracle.decode(case)
+    check_lp(o, lse, ro, rl, f"multi-token {kv} n_q={w['n_q']} lens={lens.tolist()}")
 
 
 def test_decode_fp8_every_finite_code():

@@ -134,6 +134,39 @@ def test_brute_force_decode(orc, kv, paged):
     np.testing.assert_allclose(lse[1:], lb[1:, :, 0], rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("paged", [True, False])
+def test_brute_force_multi_token_decode(orc, kv, paged):
+    """n_q = 3 query tokens per sequence, bottom-right causal against each
+    sequence's own length; lengths 0 and 2 (< n_q) leave rows with no key."""
+    lens = np.array([0, 2, 5, 16, 37], dtype=np.int32)
+    case = gen.decode_inputs(5, 4, 2, 8, lens, kv=kv, page_size=8, paged=paged, spare=3, seed=9, n_q=3)
+    o, lse = orc.decode(case)
+    K, V, L = brute.dense_kv_from_cache(case)
+    Q = brute.decode_elems(case["q"])
+    ob, lb = brute.attention(Q, K, V, causal=True, scale=case["scale"], lens=L)
+    np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lb))
+    assert np.all(np.isneginf(lse[0])) and np.all(np.isneginf(lse[1, :, 0]))  # no key: T=0, and 2 - 3 + 0 < 0
+    assert np.all(np.isfinite(lse[1, :, 1:])) and np.all(o[1, 0] == 0)
+    fin = np.isfinite(lb)
+    np.testing.assert_allclose(lse[fin], lb[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_multi_token_row_equals_single_token_on_shorter_cache(orc):
+    """Query token s of n_q is single-token decode of that query against the
+    first T - (n_q - 1 - s) keys of the same cache."""
+    lens = np.array([9, 30, 64], dtype=np.int32)
+    n_q = 4
+    case = gen.decode_inputs(3, 4, 1, 8, lens, kv="int8", page_size=16, paged=True, spare=2, seed=21, n_q=n_q)
+    o, lse = orc.decode(case)
+    for s in range(n_q):
+        one = dict(case, q=case["q"][:, s].copy(), n_q=None, lengths=lens - (n_q - 1 - s))
+        o1, l1 = orc.decode(one)
+        np.testing.assert_array_equal(o[:, s], o1)
+        np.testing.assert_array_equal(lse[:, :, s], l1)
+
+
 # ------------------------------------------------------------------ closed forms
 def test_zero_query_gives_mean_of_visible_values(orc):
     rng = np.random.default_rng(5)

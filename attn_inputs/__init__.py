@@ -111,6 +111,26 @@ def quantize_int8(x: np.ndarray):
     return q, s
 
 
+INT4_GROUP = 32  # elements per int4 scale group
+
+
+def quantize_int4(x: np.ndarray):
+    """Symmetric int4 in groups of 32 along the last axis (D): returns (uint8
+    [..., D/2] packed codes, float32 [..., D/32] scales) with
+    code = clamp(rne(x / s), -7, 7) and s = group amax / 7 (1 for an all-zero
+    group); element 2i sits in the low nibble of byte i, 2i+1 in its high
+    nibble, as 4-bit two's complement."""
+    x = np.asarray(x, dtype=np.float32)
+    *lead, D = x.shape
+    g = x.reshape(*lead, D // INT4_GROUP, INT4_GROUP)
+    amax = np.max(np.abs(g), axis=-1)
+    s = np.where(amax == 0, np.float32(1.0), amax / np.float32(7.0)).astype(np.float32)
+    q = np.clip(np.rint(g / s[..., None]), -7, 7).astype(np.int8).reshape(*lead, D)
+    u = q.view(np.uint8) & np.uint8(15)
+    packed = (u[..., 0::2] | (u[..., 1::2] << np.uint8(4))).astype(np.uint8)
+    return packed, s
+
+
 def _e4m3_grid() -> np.ndarray:
     """Non-negative finite OCP e4m3fn values for codes 0x00..0x7E, increasing."""
     vals = np.empty(127, dtype=np.float64)
@@ -181,7 +201,8 @@ def decode_inputs(B, Hq, Hkv, D, lengths, kv="bf16", page_size=512, paged=True, 
     paged:  caches [P, Hkv, page_size, D] addressed through a page table.
     contiguous: caches [B, Hkv, t_alloc, D] (t_alloc defaults to max length).
     kv: 'bf16' | 'int8' (scales shaped like the cache minus D) | 'fp8'
-        (scales [Hkv] for K and for V).
+        (scales [Hkv] for K and for V) | 'int4' (uint8 caches with D/2 bytes
+        per row, scales [.., page_size, D/32]).
     Unused cache slots are poisoned so that any stray read is visible."""
     lengths = np.asarray(lengths, dtype=np.int32)
     q = normal((B, Hq, D) if n_q is None else (B, n_q, Hq, D), seed, TID_Q, "bf16")
@@ -220,6 +241,14 @@ def decode_inputs(B, Hq, Hkv, D, lengths, kv="bf16", page_size=512, paged=True, 
             qv, s = quantize_int8(x)  # s: [P,Hkv,ps]
             bad = ~np.broadcast_to(vmask, cache_shape[:3])
             qv[bad] = 127
+            s[bad] = np.float32("nan")
+            out[name] = qv
+            out[name + "_scale"] = s
+    elif kv == "int4":
+        for name, x in (("k", kf), ("v", vf)):
+            qv, s = quantize_int4(x)  # [P,Hkv,ps,D/2], [P,Hkv,ps,D/32]
+            bad = ~np.broadcast_to(vmask, cache_shape[:3])
+            qv[bad] = 0x77
             s[bad] = np.float32("nan")
             out[name] = qv
             out[name + "_scale"] = s

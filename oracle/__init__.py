@@ -22,7 +22,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-DT = {"f32": 0, "bf16": 1, "fp8": 2, "int8": 3}
+DT = {"f32": 0, "bf16": 1, "fp8": 2, "int8": 3, "int4": 4}
 
 _lib = None
 
@@ -70,11 +70,13 @@ def _elem_kind(a: np.ndarray) -> str:
 
 
 def attention(q, k, v, *, B, Hq, Hkv, S, T, D, causal, scale, layout=0, k_scale=None, v_scale=None,
-              page_table=None, page_size=0, kv_lens=None, rows=None):
+              page_table=None, page_size=0, kv_lens=None, rows=None, kv_kind=None):
     """Exact attention in fp64 on host arrays.
 
     Element type follows the numpy dtype: float32 -> f32, uint16 -> bf16 bits,
-    uint8 -> OCP e4m3fn bytes, int8 -> int8 codes.  Returns (o, lse):
+    uint8 -> OCP e4m3fn bytes, int8 -> int8 codes; kv_kind="int4" reads uint8
+    K/V as packed int4 pairs (last dimension D/2 bytes) with per-32-element
+    group scales [.., D/32].  Returns (o, lse):
     o [B, n_rows, Hq, D], lse [B, Hq, n_rows] (float64)."""
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
@@ -89,7 +91,8 @@ def attention(q, k, v, *, B, Hq, Hkv, S, T, D, causal, scale, layout=0, k_scale=
     o = np.empty((B, n_rows, Hq, D), dtype=np.float64)
     lse = np.empty((B, Hq, n_rows), dtype=np.float64)
     max_pages = 0 if pt is None else pt.shape[1]
-    rc = load().oracle_attention(DT[_elem_kind(q)], _p(q), DT[_elem_kind(k)], layout, _p(k), _p(v), _p(ks), _p(vs),
+    kvk = kv_kind if kv_kind is not None else _elem_kind(k)
+    rc = load().oracle_attention(DT[_elem_kind(q)], _p(q), DT[kvk], layout, _p(k), _p(v), _p(ks), _p(vs),
                                  _p(pt), max_pages, page_size, _p(lens), B, Hq, Hkv, S, T, D, int(causal),
                                  float(scale), _p(rws), n_rows if rws is not None else 0, _p(o), _p(lse))
     if rc:
@@ -115,7 +118,7 @@ def decode(case):
     o, lse = attention(c["q"].reshape(c["B"], S, c["Hq"], c["D"]), c["k"], c["v"], B=c["B"], Hq=c["Hq"],
                        Hkv=c["Hkv"], S=S, T=0, D=c["D"], causal=n_q is not None, scale=c["scale"], layout=1,
                        k_scale=c.get("k_scale"), v_scale=c.get("v_scale"), page_table=c["page_table"],
-                       page_size=c["page_size"], kv_lens=c["lengths"])
+                       page_size=c["page_size"], kv_lens=c["lengths"], kv_kind=c["kv"] if c["kv"] == "int4" else None)
     if n_q is None:
         return o[:, 0], lse[:, :, 0]
     return o, lse

@@ -26,7 +26,11 @@
  *    analysis, introduction and section 1; LLM-CoOpt "Methodology" item 1
  *    (FP8 KV).  int8: value = code * per-(token, KV head) scale.  fp8: OCP
  *    e4m3fn (bias 7, no infinities, S.1111.111 = NaN) times a per-KV-head
- *    scale;
+ *    scale.  int4 (named beside int8 in the ONNX Runtime PR #28695
+ *    analysis, introduction; the layout is this build's reading): signed
+ *    two's-complement 4-bit codes, element 2i in the low nibble of byte i and
+ *    element 2i+1 in its high nibble, value = code * the scale of the
+ *    element's 32-element group of its (token, KV head) row;
  *  - merge of partial results by log-sum-exp: ONNX Runtime PR #28695
  *    analysis, section 2 (flash decoding, reduce phase).
  *
@@ -52,7 +56,9 @@ int oracle_threads(void) {
 #endif
 }
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8_E4M3 = 2, OR_INT8 = 3 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8_E4M3 = 2, OR_INT8 = 3, OR_INT4 = 4 };
+
+enum { OR_INT4_GROUP = 32 }; /* elements per int4 scale group */
 
 /* ---- element decoders, each written from its format definition ---- */
 
@@ -87,6 +93,11 @@ static double dec_elem(int dt, const void* base, int64_t idx) {
     case OR_BF16: return dec_bf16(((const uint16_t*)base)[idx]);
     case OR_FP8_E4M3: return oracle_e4m3fn_value(((const uint8_t*)base)[idx]);
     case OR_INT8: return (double)((const int8_t*)base)[idx];
+    case OR_INT4: {
+      uint8_t byte = ((const uint8_t*)base)[idx / 2];
+      int nib = (idx % 2) ? (byte >> 4) : (byte & 15);
+      return (double)(nib >= 8 ? nib - 16 : nib); /* 4-bit two's complement */
+    }
   }
   return NAN;
 }
@@ -119,6 +130,7 @@ static double kv_value(const kv_store* s, const void* base, const float* scale, 
   double x = dec_elem(s->kv_dtype, base, row * s->D + d);
   if (s->kv_dtype == OR_INT8) x *= (double)scale[row];          /* per token, per KV head */
   else if (s->kv_dtype == OR_FP8_E4M3) x *= (double)scale[hk];  /* per KV head */
+  else if (s->kv_dtype == OR_INT4) x *= (double)scale[row * (s->D / OR_INT4_GROUP) + d / OR_INT4_GROUP];
   return x;
 }
 

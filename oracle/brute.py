@@ -29,14 +29,27 @@ def decode_elems(a: np.ndarray) -> np.ndarray:
     raise TypeError(a.dtype)
 
 
+def int4_values(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Packed int4 bytes [..., D/2] and group scales [..., D/32] -> float64 [..., D]:
+    low nibble first, 4-bit two's complement, numpy bit operations."""
+    b = np.asarray(packed, dtype=np.uint8)
+    nib = np.stack([b & 0x0F, b >> 4], axis=-1).reshape(*b.shape[:-1], b.shape[-1] * 2).astype(np.int64)
+    codes = np.where(nib >= 8, nib - 16, nib).astype(np.float64)
+    group = codes.shape[-1] // np.asarray(scales).shape[-1]
+    return codes * np.repeat(np.asarray(scales, dtype=np.float64), group, axis=-1)
+
+
 def dense_kv_from_cache(case):
     """Gather a decode case's cache into dense fp64 K, V [B, Tmax, Hkv, D] plus lengths."""
     c = case
     B, Hkv, D, ps = c["B"], c["Hkv"], c["D"], c["page_size"]
     lens = np.asarray(c["lengths"], dtype=np.int64)
     tmax = int(lens.max()) if lens.size else 0
-    k = decode_elems(c["k"])  # [P, Hkv, ps, D]
-    v = decode_elems(c["v"])
+    if c["kv"] == "int4":
+        k, v = (int4_values(c[n], c[n + "_scale"]) for n in "kv")
+    else:
+        k = decode_elems(c["k"])  # [P, Hkv, ps, D]
+        v = decode_elems(c["v"])
     if c["kv"] == "int8":
         k = k * c["k_scale"].astype(np.float64)[..., None]
         v = v * c["v_scale"].astype(np.float64)[..., None]

@@ -120,27 +120,29 @@ def test_brute_force_prefill(orc, kind, causal, S, T, G):
     np.testing.assert_allclose(lse[fin], lb[fin], rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "int4"])
 @pytest.mark.parametrize("paged", [True, False])
 def test_brute_force_decode(orc, kv, paged):
     lens = np.array([0, 5, 16, 37], dtype=np.int32)
-    case = gen.decode_inputs(4, 4, 2, 8, lens, kv=kv, page_size=8, paged=paged, spare=3, seed=7)
+    D = 64 if kv == "int4" else 8  # int4 groups span 32 elements
+    case = gen.decode_inputs(4, 4, 2, D, lens, kv=kv, page_size=8, paged=paged, spare=3, seed=7)
     o, lse = orc.decode(case)
     K, V, L = brute.dense_kv_from_cache(case)
-    Q = brute.decode_elems(case["q"]).reshape(4, 1, 4, 8)
+    Q = brute.decode_elems(case["q"]).reshape(4, 1, 4, D)
     ob, lb = brute.attention(Q, K, V, causal=False, scale=case["scale"], lens=L)
     np.testing.assert_allclose(o, ob[:, 0], rtol=1e-12, atol=1e-12)
     assert np.all(np.isneginf(lse[0])) and np.all(o[0] == 0)
     np.testing.assert_allclose(lse[1:], lb[1:, :, 0], rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "int4"])
 @pytest.mark.parametrize("paged", [True, False])
 def test_brute_force_multi_token_decode(orc, kv, paged):
     """n_q = 3 query tokens per sequence, bottom-right causal against each
     sequence's own length; lengths 0 and 2 (< n_q) leave rows with no key."""
     lens = np.array([0, 2, 5, 16, 37], dtype=np.int32)
-    case = gen.decode_inputs(5, 4, 2, 8, lens, kv=kv, page_size=8, paged=paged, spare=3, seed=9, n_q=3)
+    case = gen.decode_inputs(5, 4, 2, 32 if kv == "int4" else 8, lens, kv=kv, page_size=8, paged=paged, spare=3,
+                             seed=9, n_q=3)
     o, lse = orc.decode(case)
     K, V, L = brute.dense_kv_from_cache(case)
     Q = brute.decode_elems(case["q"])
@@ -151,6 +153,49 @@ def test_brute_force_multi_token_decode(orc, kv, paged):
     assert np.all(np.isfinite(lse[1, :, 1:])) and np.all(o[1, 0] == 0)
     fin = np.isfinite(lb)
     np.testing.assert_allclose(lse[fin], lb[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_int4_codes_decode_to_twos_complement_nibbles(orc):
+    """A zero query and zero keys weigh every key alike, so O is the mean of the
+    values.  With V's bytes covering all 256 (low, high) nibble pairs and unit
+    scales, each output element is the mean of 4-bit two's-complement codes
+    written out here from the definition: nibble n -> n if n < 8 else n - 16."""
+    D, T = 64, 256
+    nib_value = {n: (n if n < 8 else n - 16) for n in range(16)}
+    vbytes = np.zeros((1, 1, T, D // 2), dtype=np.uint8)
+    for t in range(T):
+        vbytes[0, 0, t, :] = (t + np.arange(D // 2)) % 256  # token t, byte i: (t + i) mod 256
+    expect = np.zeros(D)
+    for i in range(D // 2):
+        vals = [(t + i) % 256 for t in range(T)]
+        expect[2 * i] = np.mean([nib_value[b & 15] for b in vals])
+        expect[2 * i + 1] = np.mean([nib_value[b >> 4] for b in vals])
+    kbytes = np.zeros_like(vbytes)
+    ones = np.ones((1, 1, T, D // 32), dtype=np.float32)
+    q = np.zeros((1, 1, 1, D), dtype=np.uint16)
+    o, lse = orc.attention(q, kbytes, vbytes, B=1, Hq=1, Hkv=1, S=1, T=0, D=D, causal=False, scale=0.125, layout=1,
+                           k_scale=ones, v_scale=ones, page_size=T, kv_lens=np.array([T]), kv_kind="int4")
+    np.testing.assert_allclose(o[0, 0, 0], expect, rtol=0, atol=1e-12)
+    assert abs(lse[0, 0, 0] - np.log(T)) < 1e-12  # T equal scores of 0
+    # a group's scale multiplies exactly its 32 elements
+    sc = np.ones((1, 1, T, D // 32), dtype=np.float32)
+    sc[..., 1] = 2.0
+    o2, _ = orc.attention(q, kbytes, vbytes, B=1, Hq=1, Hkv=1, S=1, T=0, D=D, causal=False, scale=0.125, layout=1,
+                          k_scale=ones, v_scale=sc, page_size=T, kv_lens=np.array([T]), kv_kind="int4")
+    np.testing.assert_allclose(o2[0, 0, 0], expect * np.repeat([1.0, 2.0], 32), rtol=0, atol=1e-12)
+
+
+def test_int4_quantizer_roundtrip():
+    x = gen.normal((3, 5, 128), 11, gen.TID_K, "f32")
+    x[0, 0, :32] = 0.0  # an all-zero group
+    packed, s = gen.quantize_int4(x)
+    assert packed.shape == (3, 5, 64) and s.shape == (3, 5, 4)
+    vals = brute.int4_values(packed, s)
+    err = np.abs(vals - x.astype(np.float64))
+    assert np.all(err <= np.repeat(s, 32, axis=-1) / 2 + 1e-6)
+    nib = np.concatenate([packed & 15, packed >> 4], axis=-1)
+    assert not np.any(nib == 8)  # codes stay in [-7, 7]
+    assert np.all(vals[0, 0, :32] == 0) and s[0, 0, 0] == 1.0
 
 
 def test_multi_token_row_equals_single_token_on_shorter_cache(orc):

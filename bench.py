@@ -8,8 +8,8 @@ only unmasked (query, key) pairs at 4*D flop each.  Beside it, in the same run:
     D=128, 512-token pages, ragged lengths U[1024, 32768]) in GB/s of KV bytes
     of valid tokens (+ q, o, lse), with the cache copies rotated so each
     timed launch streams from HBM rather than from the 256 MB last-level cache;
-  * ``decode_quant``: the same decode over contiguous int8 and OCP e4m3fn
-    caches (B=4, Hq=32, Hkv=8, D=128, T=65536) in GB/s of cache bytes;
+  * ``decode_quant``: the same decode over contiguous int8, OCP e4m3fn and
+    int4 caches (B=4, Hq=32, Hkv=8, D=128, T=65536) in GB/s of cache bytes;
   * ``decode_multi``: multi-token decode (n_q=4 verified tokens per sequence)
     over paged bf16 and int8 caches of the decode workload's shape, in GB/s;
   * ``roofline`` / ``decode.roofline``: achieved vs MI355X peak, timed with HIP
@@ -180,7 +180,8 @@ def bench_decode(args):
 def bench_decode_quant(args):
     """Quantised-cache decode (B=4, Hq=32, Hkv=8, D=128, T=65536 for every
     sequence, contiguous cache): int8 codes with per-(token, KV head) scales,
-    and OCP e4m3fn codes with per-KV-head scales.  The codes are seeded
+    OCP e4m3fn codes with per-KV-head scales, and packed int4 codes with one
+    scale per 32-element group.  The codes are seeded
     synthetic draws made on the device (parity on the same shapes is the
     GPU test suite's job); GB/s counts the cache bytes (codes + int8 scales)."""
     import torch
@@ -199,13 +200,18 @@ def bench_decode_quant(args):
     lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     res = {}
-    for kv in ("int8", "fp8"):
-        shape = (B, Hkv, T, D)
-        code_bytes = B * Hkv * T * D * 2
+    for kv in ("int8", "fp8", "int4"):
+        shape = (B, Hkv, T, D // 2 if kv == "int4" else D)
+        code_bytes = B * Hkv * T * shape[-1] * 2
         copies = max(2, math.ceil((1 << 30) / code_bytes))
         caches = []
         for _ in range(copies):
-            if kv == "int8":
+            if kv == "int4":
+                k = torch.randint(0, 256, shape, generator=g, dtype=torch.uint8, device="cuda")
+                v = torch.randint(0, 256, shape, generator=g, dtype=torch.uint8, device="cuda")
+                ks = torch.rand((B, Hkv, T, D // 32), generator=g, device="cuda") * 0.02 + 0.005
+                vs = torch.rand((B, Hkv, T, D // 32), generator=g, device="cuda") * 0.02 + 0.005
+            elif kv == "int8":
                 k = torch.randint(-127, 128, shape, generator=g, dtype=torch.int8, device="cuda")
                 v = torch.randint(-127, 128, shape, generator=g, dtype=torch.int8, device="cuda")
                 ks = torch.rand((B, Hkv, T), generator=g, device="cuda") * 0.02 + 0.005
@@ -219,18 +225,21 @@ def bench_decode_quant(args):
 
         def step(i, caches=caches, copies=copies):
             k, v, ks, vs = caches[i % copies]
-            attn.decode_splitkv(q, k, v, lens, T, k_scale=ks, v_scale=vs, workspace=ws, out=o, lse=lse)
+            attn.decode_splitkv(q, k, v, lens, T, k_scale=ks, v_scale=vs, workspace=ws, out=o, lse=lse,
+                                kv_dtype="int4" if kv == "int4" else None)
 
         steps = max(args.steps, copies * 4)
         ms = timed(step, steps, max(args.warmup, copies), stream)
-        nbytes = code_bytes + (B * Hkv * T * 4 * 2 if kv == "int8" else 0)
+        scale_bytes = {"int8": B * Hkv * T * 4 * 2, "int4": B * Hkv * T * (D // 32) * 4 * 2}.get(kv, 0)
+        nbytes = code_bytes + scale_bytes
         gbs = nbytes / (ms * 1e-3) / 1e9
         log(f"decode {kv}: {ms * 1e3:.2f} us/call, {gbs:.1f} GB/s ({nbytes / 1e6:.1f} MB)")
         res[kv] = {"value": round(gbs, 2), "unit": "GB/s", "us_per_call": round(ms * 1e3, 3), "bytes": nbytes,
                    "cache_copies": copies, "steps": steps,
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                "traffic": recorded_traffic(f"decode_{kv}_contig_pmc_traffic.md", "decode.hip")}}
+                                "traffic": recorded_traffic(f"decode_{kv}_contig_pmc_traffic.md", "decode.hip")
+                                if kv != "int4" else None}}
         del caches
     return {"workload": "quant_decode", "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "T": T, "kv": res}
 

@@ -10,7 +10,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "lib", "libattn.so")
 
-ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3, ATTN_INT8 = 0, 1, 2, 3
+ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3, ATTN_INT8, ATTN_INT4 = 0, 1, 2, 3, 4
 _STATUS = {0: "ATTN_OK", 1: "ATTN_E_INVALID", 2: "ATTN_E_UNSUPPORTED", 3: "ATTN_E_BUDGET", 4: "ATTN_E_DEVICE"}
 
 
@@ -135,6 +135,10 @@ def decode_workspace_size(B, Hq, Hkv, D, max_kv_len, num_splits=0) -> int:
 
 
 def _cache_dtype(k_cache, kv_dtype):
+    if kv_dtype == "int4":
+        if k_cache.dtype != torch.uint8:
+            raise ValueError("int4 caches are uint8 tensors of packed nibble pairs")
+        return ATTN_INT4
     if kv_dtype == "fp8" or k_cache.dtype == torch.float8_e4m3fn:
         return ATTN_FP8_E4M3
     if k_cache.dtype == torch.int8:
@@ -148,7 +152,8 @@ def decode_splitkv(q, k_cache, v_cache, kv_lens, max_kv_len, *, page_table=None,
                    kv_dtype=None, scale=None, num_splits=0, workspace=None, out=None, lse=None, return_lse=True):
     """Split-KV decode.  q [B,Hq,D] bf16; caches [P,Hkv,page,D] (paged) or
     [B,Hkv,page,D] (contiguous) of bf16 / int8 / float8_e4m3fn (uint8 bytes
-    with kv_dtype='fp8').  Returns (o [B,Hq,D] fp32, lse [B,Hq] or None)."""
+    with kv_dtype='fp8'), or uint8 [..., D/2] packed int4 with kv_dtype='int4'
+    (scales [..., page, D/32]).  Returns (o [B,Hq,D] fp32, lse [B,Hq] or None)."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (kv_lens, "kv_lens")):
         _need(t, n)
     kdt = _cache_dtype(k_cache, kv_dtype)

@@ -104,8 +104,9 @@ attn_status decode_impl(attn_dtype kv_dt, const void* q, const void* k_cache, co
                         int page_size, int num_pages, const int32_t* kv_lens, int max_kv_len, int B, int n_q, int Hq,
                         int Hkv, int D, float scale, int num_splits, void* workspace, size_t workspace_bytes,
                         float* o, float* lse, void* stream) {
-  if (kv_dt != ATTN_BF16 && kv_dt != ATTN_INT8 && kv_dt != ATTN_FP8_E4M3)
-    return set_error(ATTN_E_UNSUPPORTED, "decode: KV dtype must be bf16, int8 or fp8 e4m3 (got %d)", (int)kv_dt);
+  if (kv_dt != ATTN_BF16 && kv_dt != ATTN_INT8 && kv_dt != ATTN_FP8_E4M3 && kv_dt != ATTN_INT4)
+    return set_error(ATTN_E_UNSUPPORTED, "decode: KV dtype must be bf16, int8, fp8 e4m3 or int4 (got %d)",
+                     (int)kv_dt);
   if (D != 64 && D != 128) return set_error(ATTN_E_UNSUPPORTED, "decode: D must be 64 or 128 (got %d)", D);
   if (B < 0 || Hq <= 0 || Hkv <= 0 || max_kv_len < 0 || num_splits < 0 || n_q <= 0)
     return set_error(ATTN_E_INVALID, "decode: invalid sizes");

@@ -20,12 +20,14 @@
 // The caches may be paged (fixed-size pages located through a page table:
 // LLM-CoOpt, "Methodology" item 3) and quantised (int8 with a per-token,
 // per-KV-head scale; OCP e4m3fn with a per-KV-head scale: LLM-CoOpt
-// "Methodology" item 1, ONNX Runtime PR #28695 analysis, section 1); bytes are
-// dequantised in registers right after the 16-byte loads.
+// "Methodology" item 1, ONNX Runtime PR #28695 analysis, section 1; int4
+// codes packed two per byte with one scale per 32-element group: the same
+// analysis, introduction); bytes are dequantised in registers right after the
+// loads.
 //
 // This is a bandwidth-bound scan, so the vector ALUs do the arithmetic.  The
-// lanes of a wave form token slots of D*bytes/16 lanes, each lane owning one
-// 16-byte slice of a token's K and V rows; every iteration a wave loads the K
+// lanes of a wave form token slots, each lane owning one slice of a token's K
+// and V rows (16 bytes; 8 bytes = 16 elements for int4); every iteration a wave loads the K
 // and V slices of 4 tokens per slot (all loads in flight together), reduces
 // the slice dot products across the slot with row-local DPP moves, and
 // folds the tokens into a per-slot online softmax (running max, sum and
@@ -47,47 +49,76 @@
 namespace attn {
 namespace {
 
+// A lane's slice of a token's K or V row: 16 bytes (8 bf16, 16 e4m3 or 16
+// int8 elements) or, for int4, 8 bytes (16 packed elements, so that a lane
+// holds as many elements, and accumulators, as for the 8-bit types).
 template <int KV>
 struct KvTraits;
 template <>
 struct KvTraits<ATTN_BF16> {
-  static constexpr int kBytes = 2;
+  using Slice = uint4;
+  static constexpr int kEpl = 8;
+  static constexpr int row_bytes(int D) { return 2 * D; }
 };
 template <>
 struct KvTraits<ATTN_FP8_E4M3> {
-  static constexpr int kBytes = 1;
+  using Slice = uint4;
+  static constexpr int kEpl = 16;
+  static constexpr int row_bytes(int D) { return D; }
 };
 template <>
 struct KvTraits<ATTN_INT8> {
-  static constexpr int kBytes = 1;
+  using Slice = uint4;
+  static constexpr int kEpl = 16;
+  static constexpr int row_bytes(int D) { return D; }
 };
+template <>
+struct KvTraits<ATTN_INT4> {
+  using Slice = uint2;
+  static constexpr int kEpl = 16;
+  static constexpr int row_bytes(int D) { return D / 2; }
+};
+constexpr int kInt4Group = 32;  // elements per int4 scale group
 
-// Decode one 16-byte slice into EPL floats (without scales).
+// The 4-bit two's-complement code at nibble e (element e of the word: bits
+// 4e .. 4e+3, low nibble of a byte first) as an int.
+__device__ __forceinline__ int int4_code(uint32_t w, int e) { return __builtin_amdgcn_sbfe((int)w, 4 * e, 4); }
+
+// Decode one slice into EPL floats (without scales).
 template <int KV>
-__device__ __forceinline__ void decode16(uint4 raw, float* out) {
-  const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-  if constexpr (KV == ATTN_BF16) {
+__device__ __forceinline__ void decode_slice(const typename KvTraits<KV>::Slice& raw, float* out) {
+  if constexpr (KV == ATTN_INT4) {
+    const uint32_t wd[2] = {raw.x, raw.y};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[2 * i] = __uint_as_float(wd[i] << 16);
-      out[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
-    }
-  } else if constexpr (KV == ATTN_FP8_E4M3) {
-    // gfx950 converts OCP e4m3fn in hardware, two bytes per instruction
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], false);
-      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], true);
-      out[4 * i] = lo[0];
-      out[4 * i + 1] = lo[1];
-      out[4 * i + 2] = hi[0];
-      out[4 * i + 3] = hi[1];
+      for (int e = 0; e < 8; ++e) out[8 * i + e] = (float)int4_code(wd[i], e);
     }
   } else {
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+    if constexpr (KV == ATTN_BF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(wd[i] << 16);
+        out[2 * i + 1] = __uint_as_float(wd[i] & 0xffff0000u);
+      }
+    } else if constexpr (KV == ATTN_FP8_E4M3) {
+      // gfx950 converts OCP e4m3fn in hardware, two bytes per instruction
 #pragma unroll
-      for (int k = 0; k < 4; ++k) out[4 * i + k] = (float)(int)(int8_t)(wd[i] >> (8 * k));
+      for (int i = 0; i < 4; ++i) {
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], false);
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], true);
+        out[4 * i] = lo[0];
+        out[4 * i + 1] = lo[1];
+        out[4 * i + 2] = hi[0];
+        out[4 * i + 3] = hi[1];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[4 * i + k] = (float)(int)(int8_t)(wd[i] >> (8 * k));
+      }
     }
   }
 }
@@ -105,31 +136,45 @@ __device__ __forceinline__ float token_sum(float x) {
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
-// One 16-byte K slice as EPL/2 exact bf16 pairs, the operand of the packed
-// bf16 dot product: every e4m3fn value and every int8 code is a bf16 number.
+// One K slice as EPL/2 exact bf16 pairs, the operand of the packed bf16 dot
+// product: every e4m3fn value and every int8 / int4 code is a bf16 number.
 // e4m3fn goes through gfx950's scaled fp8 -> bf16 pair conversion (scale 1);
-// int8 through fp32, whose upper half is then the exact bf16.
+// int8 and int4 through fp32, whose upper half is then the exact bf16.
 template <int KV>
-__device__ __forceinline__ void k_pairs(uint4 raw, bf16x2* out) {
-  const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-  if constexpr (KV == ATTN_BF16) {
+__device__ __forceinline__ void k_pairs(const typename KvTraits<KV>::Slice& raw, bf16x2* out) {
+  if constexpr (KV == ATTN_INT4) {
+    const uint32_t wd[2] = {raw.x, raw.y};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = __builtin_bit_cast(bf16x2, wd[i]);
-  } else if constexpr (KV == ATTN_FP8_E4M3) {
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd[i], 1.0f, false);
-      out[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd[i], 1.0f, true);
+      for (int e = 0; e < 8; e += 2) {
+        const float f0 = (float)int4_code(wd[i], e);
+        const float f1 = (float)int4_code(wd[i], e + 1);
+        out[4 * i + e / 2] = __builtin_bit_cast(
+            bf16x2, __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u));
+      }
     }
   } else {
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+    if constexpr (KV == ATTN_BF16) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) out[i] = __builtin_bit_cast(bf16x2, wd[i]);
+    } else if constexpr (KV == ATTN_FP8_E4M3) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const float f0 = (float)(int)(int8_t)(wd[i] >> (16 * hf));
-        const float f1 = (float)(int)(int8_t)(wd[i] >> (16 * hf + 8));
-        out[2 * i + hf] = __builtin_bit_cast(
-            bf16x2, __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u));
+      for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd[i], 1.0f, false);
+        out[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)wd[i], 1.0f, true);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const float f0 = (float)(int)(int8_t)(wd[i] >> (16 * hf));
+          const float f1 = (float)(int)(int8_t)(wd[i] >> (16 * hf + 8));
+          out[2 * i + hf] = __builtin_bit_cast(
+              bf16x2, __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u));
+        }
       }
     }
   }
@@ -220,8 +265,9 @@ constexpr int kDecodeThreads = 64 * kDecodeWaves;
 // the piece's K/V right after the first, from the caches.
 template <int KV, int D, int G, int TQ>
 __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs a) {
-  constexpr int EB = KvTraits<KV>::kBytes;
-  constexpr int EPL = 16 / EB;   // elements per lane slice
+  using Tr = KvTraits<KV>;
+  using Slice = typename Tr::Slice;
+  constexpr int EPL = Tr::kEpl;  // elements per lane slice
   constexpr int LPT = D / EPL;   // lanes per token
   constexpr int TPW = 64 / LPT;  // tokens per wave per load step (token slots)
   constexpr int U = 4;           // load steps per iteration
@@ -240,7 +286,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
   const int wu = __builtin_amdgcn_readfirstlane(w);  // wave index as a scalar
   const uint8_t* kb = (const uint8_t*)a.k;
   const uint8_t* vb = (const uint8_t*)a.v;
-  const int64_t lane_off = (int64_t)part * EPL * EB;
+  const int64_t lane_off = (int64_t)part * sizeof(Slice);
+  constexpr int64_t RB = Tr::row_bytes(D);  // bytes of one token's K (or V) row
   constexpr int kStride = kDecodeWaves * TPI;  // tokens between a wave's consecutive iterations
 
   group_prefix<kDecodeThreads>(a.kv_lens, a.B, a.max_kv_len, pre, wsum);
@@ -318,7 +365,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
     // from a TPW-aligned index never straddle a page and every step index is
     // wave-uniform, so the page-table entries are scalar loads issued first.
     struct Buf {
-      uint4 kr[U], vr[U];
+      Slice kr[U], vr[U];
       float ksc[U], vsc[U];
     };
     // Every call issues the same number of vector loads with no branch around
@@ -347,11 +394,15 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t row = step_row[u] + min(g0 + u * TPW + slot, tend - 1);
-        bf.kr[u] = *(const uint4*)(kb + row * (D * EB) + lane_off);
-        bf.vr[u] = *(const uint4*)(vb + row * (D * EB) + lane_off);
+        bf.kr[u] = *(const Slice*)(kb + row * RB + lane_off);
+        bf.vr[u] = *(const Slice*)(vb + row * RB + lane_off);
         if constexpr (KV == ATTN_INT8) {
           bf.ksc[u] = a.k_scale[row];  // q already carries scale*log2(e)
           bf.vsc[u] = a.v_scale[row];
+        } else if constexpr (KV == ATTN_INT4) {
+          // the scale of this lane's 32-element group (two lane slices per group)
+          bf.ksc[u] = a.k_scale[row * (D / kInt4Group) + (part * EPL) / kInt4Group];
+          bf.vsc[u] = a.v_scale[row * (D / kInt4Group) + (part * EPL) / kInt4Group];
         } else {
           bf.ksc[u] = bf.vsc[u] = 1.f;
         }
@@ -369,6 +420,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
           float d = 0.f;
 #pragma unroll
           for (int i = 0; i < EPL / 2; ++i) d = __builtin_amdgcn_fdot2_f32_bf16(q2[g][i], kp[i], d, false);
+          if constexpr (KV == ATTN_INT4) d *= bf.ksc[u];  // a group scale differs between lanes
           s[u][g] = d;
         }
 #pragma unroll
@@ -387,7 +439,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
       }
       float vv[U][EPL];
 #pragma unroll
-      for (int u = 0; u < U; ++u) decode16<KV>(bf.vr[u], vv[u]);
+      for (int u = 0; u < U; ++u) decode_slice<KV>(bf.vr[u], vv[u]);
       // Scores enter the softmax as s*smul (log2 domain, smul > 0).  The
       // reference max m of a slot only moves when a score exceeds it by more
       // than 8, so p <= 256 and the rescale of the accumulators is skipped
@@ -422,7 +474,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
         for (int u = 0; u < U; ++u) {
           p[u] = __builtin_amdgcn_exp2f(fmaf(s[u][g], smul, nm));
           l[g] += p[u];
-          if constexpr (KV == ATTN_INT8) p[u] *= bf.vsc[u];
+          if constexpr (KV == ATTN_INT8 || KV == ATTN_INT4) p[u] *= bf.vsc[u];
         }
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
@@ -680,6 +732,7 @@ attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a, int D, int G, h
     case ATTN_BF16: return launch_d<ATTN_BF16>(a, D, G, stream);
     case ATTN_FP8_E4M3: return launch_d<ATTN_FP8_E4M3>(a, D, G, stream);
     case ATTN_INT8: return launch_d<ATTN_INT8>(a, D, G, stream);
+    case ATTN_INT4: return launch_d<ATTN_INT4>(a, D, G, stream);
     default: break;
   }
   return set_error(ATTN_E_UNSUPPORTED, "decode: unsupported KV dtype %d", (int)kv_dt);

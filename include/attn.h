@@ -54,7 +54,10 @@ typedef enum attn_dtype {
   ATTN_F32 = 0,       /* IEEE binary32 */
   ATTN_BF16 = 1,      /* bfloat16 (upper half of binary32) */
   ATTN_FP8_E4M3 = 2,  /* OCP 8-bit E4M3 "fn": bias 7, no infinities, 0x7F/0xFF are NaN */
-  ATTN_INT8 = 3       /* signed 8-bit code, value = code * scale */
+  ATTN_INT8 = 3,      /* signed 8-bit code, value = code * scale */
+  ATTN_INT4 = 4       /* signed 4-bit two's-complement codes, two per byte (element 2i in the low
+                         nibble of byte i, 2i+1 in the high nibble); value = code * the scale of
+                         the element's 32-element group.  KV caches of attn_decode_* only. */
 } attn_dtype;
 
 /*
@@ -90,19 +93,21 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len,
  * of a sequence yields a normalised partial output and its lse, and the
  * pieces are merged exactly by log-sum-exp.  (Flash decoding: ONNX Runtime PR #28695
  * analysis, section 2; 512-token pages: LLM-CoOpt "Methodology" item 3;
- * FP8 / INT8 caches dequantised on the fly: LLM-CoOpt "Methodology" item 1,
- * ONNX Runtime PR #28695 analysis, introduction and section 1.)
+ * FP8 / INT8 / INT4 caches dequantised on the fly: LLM-CoOpt "Methodology"
+ * item 1, ONNX Runtime PR #28695 analysis, introduction and section 1.)
  *
- *   kv_dt       ATTN_BF16, ATTN_INT8 or ATTN_FP8_E4M3 (element type of the caches)
+ *   kv_dt       ATTN_BF16, ATTN_INT8, ATTN_FP8_E4M3 or ATTN_INT4 (element type of the caches)
  *   q           device, [B, Hq, D] bf16
  *   k_cache,
  *   v_cache     device.  Paged (page_table != NULL): [num_pages, Hkv, page_size, D].
  *               Contiguous (page_table == NULL): [B, Hkv, page_size, D], i.e.
  *               one page of page_size >= max_kv_len tokens per sequence.
+ *               int4: the last dimension is D/2 bytes.
  *   k_scale,
  *   v_scale     device fp32.  int8: per token and KV head, shaped like the
  *               cache without D ([num_pages or B, Hkv, page_size]).
- *               fp8: per KV head, [Hkv].  bf16: NULL.
+ *               fp8: per KV head, [Hkv].  int4: per 32-element group,
+ *               [num_pages or B, Hkv, page_size, D/32].  bf16: NULL.
  *   page_table  device int32 [B, max_pages]: physical page of logical page
  *               t / page_size of sequence b; entries past the sequence's
  *               last page are never read.  Paged mode needs page_size a power

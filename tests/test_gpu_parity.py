@@ -170,7 +170,7 @@ def gpu_decode(case, num_splits=0):
     maxlen = int(case["lengths"].max()) if len(case["lengths"]) else 0
     fn = attn.decode_multi if case.get("n_q") is not None else attn.decode_splitkv
     o, lse = fn(q, k, v, lens, maxlen, page_table=pt, k_scale=ks, v_scale=vs,
-                kv_dtype="fp8" if kind == "fp8" else None, scale=case["scale"], num_splits=num_splits)
+                kv_dtype=kind if kind in ("fp8", "int4") else None, scale=case["scale"], num_splits=num_splits)
     torch.cuda.synchronize()
     return o.cpu().numpy(), lse.cpu().numpy()
 
@@ -187,10 +187,11 @@ def test_decode_paged_splitkv_bf16_full():
     check_lp(o, lse, ro, rl, f"paged bf16 decode lens={lens.tolist()}")
 
 
-@pytest.mark.parametrize("kv", ["int8", "fp8"])
+@pytest.mark.parametrize("kv", ["int8", "fp8", "int4"])
 @pytest.mark.parametrize("T", [4096, 65536])
 def test_decode_quantised_full(kv, T):
-    """B=4 Hq=32 Hkv=8 D=128, contiguous int8 (per-token-per-head scales) or fp8 e4m3 (per-head scales)."""
+    """B=4 Hq=32 Hkv=8 D=128, contiguous int8 (per-token-per-head scales), fp8 e4m3 (per-head
+    scales) or int4 (packed nibbles, per-32-element-group scales)."""
     import oracle
     w = gen.WORKLOADS["quant_decode"]
     lens = np.full(w["B"], T, dtype=np.int32)
@@ -201,7 +202,7 @@ def test_decode_quantised_full(kv, T):
     check_lp(o, lse, ro, rl, f"{kv} decode T={T}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "int4"])
 @pytest.mark.parametrize("paged,page_size", [(True, 16), (True, 512), (False, 0)])
 @pytest.mark.parametrize("G,D", [(1, 128), (4, 64), (5, 128), (8, 128)])
 def test_decode_ragged_edge_cases(kv, paged, page_size, G, D):
@@ -231,7 +232,7 @@ def test_decode_many_sequences_mixed_lengths():
         check_lp(o, lse, ro, rl, f"B=300 mixed lengths units={ns}")
 
 
-@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8"])
+@pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "int4"])
 @pytest.mark.parametrize("G,n_q,D", [(4, 2, 128), (4, 4, 128), (1, 8, 128), (2, 3, 64), (5, 2, 128), (8, 3, 128),
                                      (1, 13, 64)])
 def test_decode_multi_token_edge_cases(kv, G, n_q, D):

@@ -162,8 +162,27 @@ def encode_e4m3fn(y: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------- workloads
+def quantize_e4m3_per_head(x: np.ndarray, head_axis: int):
+    """e4m3fn bytes with one fp32 scale per head: s = amax / 448 over the
+    head's elements (1 for an all-zero head)."""
+    x = np.asarray(x, dtype=np.float32)
+    axes = tuple(a for a in range(x.ndim) if a != head_axis)
+    amax = np.max(np.abs(x), axis=axes) if x.size else np.zeros(x.shape[head_axis], np.float32)
+    s = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    shape = [1] * x.ndim
+    shape[head_axis] = -1
+    return encode_e4m3fn(x / s.reshape(shape)), s
+
+
 def prefill_inputs(B, Hq, Hkv, S, T, D, kind="bf16", seed=0x5EED):
-    """Dense prefill operands: Q [B,S,Hq,D], K,V [B,T,Hkv,D]."""
+    """Dense prefill operands: Q [B,S,Hq,D], K,V [B,T,Hkv,D].  kind 'fp8':
+    e4m3fn bytes with per-head scales q_scale [Hq], k_scale / v_scale [Hkv]."""
+    if kind == "fp8":
+        out = {"B": B, "Hq": Hq, "Hkv": Hkv, "S": S, "T": T, "D": D, "kind": kind, "scale": 1.0 / math.sqrt(D)}
+        for name, shape, tid in (("q", (B, S, Hq, D), TID_Q), ("k", (B, T, Hkv, D), TID_K),
+                                 ("v", (B, T, Hkv, D), TID_V)):
+            out[name], out[name + "_scale"] = quantize_e4m3_per_head(normal(shape, seed, tid, "f32"), 2)
+        return out
     q = normal((B, S, Hq, D), seed, TID_Q, kind)
     k = normal((B, T, Hkv, D), seed, TID_K, kind)
     v = normal((B, T, Hkv, D), seed, TID_V, kind)

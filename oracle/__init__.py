@@ -45,7 +45,7 @@ def load():
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
-        lib.oracle_attention.argtypes = [ctypes.c_int, P, ctypes.c_int, ctypes.c_int, P, P, P, P, P, I64, I64, P,
+        lib.oracle_attention.argtypes = [ctypes.c_int, P, P, ctypes.c_int, ctypes.c_int, P, P, P, P, P, I64, I64, P,
                                          I64, I64, I64, I64, I64, I64, ctypes.c_int, ctypes.c_double, P, I64, P, P]
         lib.oracle_attention.restype = ctypes.c_int
         lib.oracle_merge.argtypes = [I64, P, P, I64, I64, P, P]
@@ -70,13 +70,15 @@ def _elem_kind(a: np.ndarray) -> str:
 
 
 def attention(q, k, v, *, B, Hq, Hkv, S, T, D, causal, scale, layout=0, k_scale=None, v_scale=None,
-              page_table=None, page_size=0, kv_lens=None, rows=None, kv_kind=None):
+              page_table=None, page_size=0, kv_lens=None, rows=None, kv_kind=None, q_scale=None):
     """Exact attention in fp64 on host arrays.
 
     Element type follows the numpy dtype: float32 -> f32, uint16 -> bf16 bits,
     uint8 -> OCP e4m3fn bytes, int8 -> int8 codes; kv_kind="int4" reads uint8
     K/V as packed int4 pairs (last dimension D/2 bytes) with per-32-element
-    group scales [.., D/32].  Returns (o, lse):
+    group scales [.., D/32].  q_scale [Hq] (optional) multiplies query head h;
+    k_scale / v_scale [Hkv] are per-KV-head scales of e4m3 K/V in either
+    layout.  Returns (o, lse):
     o [B, n_rows, Hq, D], lse [B, Hq, n_rows] (float64)."""
     q = np.ascontiguousarray(q)
     k = np.ascontiguousarray(k)
@@ -92,7 +94,8 @@ def attention(q, k, v, *, B, Hq, Hkv, S, T, D, causal, scale, layout=0, k_scale=
     lse = np.empty((B, Hq, n_rows), dtype=np.float64)
     max_pages = 0 if pt is None else pt.shape[1]
     kvk = kv_kind if kv_kind is not None else _elem_kind(k)
-    rc = load().oracle_attention(DT[_elem_kind(q)], _p(q), DT[kvk], layout, _p(k), _p(v), _p(ks), _p(vs),
+    qsc = None if q_scale is None else np.ascontiguousarray(q_scale, dtype=np.float32)
+    rc = load().oracle_attention(DT[_elem_kind(q)], _p(q), _p(qsc), DT[kvk], layout, _p(k), _p(v), _p(ks), _p(vs),
                                  _p(pt), max_pages, page_size, _p(lens), B, Hq, Hkv, S, T, D, int(causal),
                                  float(scale), _p(rws), n_rows if rws is not None else 0, _p(o), _p(lse))
     if rc:
@@ -101,10 +104,12 @@ def attention(q, k, v, *, B, Hq, Hkv, S, T, D, causal, scale, layout=0, k_scale=
 
 
 def prefill(case, causal=True, rows=None):
-    """Oracle for a dense prefill case built by attn_inputs.prefill_inputs."""
+    """Oracle for a dense prefill case built by attn_inputs.prefill_inputs
+    (e4m3 cases carry per-head q/k/v scales)."""
     c = case
     return attention(c["q"], c["k"], c["v"], B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], S=c["S"], T=c["T"], D=c["D"],
-                     causal=causal, scale=c["scale"], rows=rows)
+                     causal=causal, scale=c["scale"], rows=rows, q_scale=c.get("q_scale"),
+                     k_scale=c.get("k_scale"), v_scale=c.get("v_scale"))
 
 
 def decode(case):

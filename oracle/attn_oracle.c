@@ -167,7 +167,8 @@ static void one_row(const kv_store* s, const double* qv, int64_t b, int64_t hk, 
 
 /*
  * Attention in fp64.
- *   q: [B, S, Hq, D] of q_dtype (f32 or bf16 bits).
+ *   q: [B, S, Hq, D] of q_dtype (f32, bf16 bits or e4m3fn bytes); q_scale [Hq]
+ *      (nullable) multiplies query head h (the per-head scale of e4m3 queries).
  *   KV (prefill layout, layout=0): k, v [B, T, Hkv, D]; kv_lens may be NULL (all T).
  *   KV (cache layout,  layout=1): k, v [P, Hkv, page_size, D] through page_table
  *       [B, max_pages] int32, or contiguous [B, Hkv, page_size, D] when
@@ -178,7 +179,8 @@ static void one_row(const kv_store* s, const double* qv, int64_t b, int64_t hk, 
  *   Out: o [B, n_rows, Hq, D] f64, lse [B, Hq, n_rows] f64.
  * Returns 0 on success, nonzero on bad arguments or allocation failure.
  */
-int oracle_attention(int q_dtype, const void* q, int kv_dtype, int layout, const void* k, const void* v,
+int oracle_attention(int q_dtype, const void* q, const float* q_scale, int kv_dtype, int layout, const void* k,
+                     const void* v,
                      const float* k_scale, const float* v_scale, const int32_t* page_table, int64_t max_pages,
                      int64_t page_size, const int64_t* kv_lens, int64_t B, int64_t Hq, int64_t Hkv, int64_t S,
                      int64_t T, int64_t D, int causal, double scale, const int64_t* rows, int64_t n_rows,
@@ -215,7 +217,8 @@ int oracle_attention(int q_dtype, const void* q, int kv_dtype, int layout, const
           int64_t last = i + Tb - S; /* last visible key index */
           n_vis = last + 1 < Tb ? last + 1 : Tb;
         }
-        for (int64_t d = 0; d < D; ++d) qv[d] = dec_elem(q_dtype, q, ((b * S + i) * Hq + h) * D + d);
+        double qs = q_scale ? (double)q_scale[h] : 1.0;
+        for (int64_t d = 0; d < D; ++d) qv[d] = qs * dec_elem(q_dtype, q, ((b * S + i) * Hq + h) * D + d);
         one_row(&st, qv, b, hk, n_vis, scale, scratch, o + ((b * n_rows + r) * Hq + h) * D,
                 lse + (b * Hq + h) * n_rows + r);
       }

@@ -105,7 +105,7 @@ def test_golden_closed_forms(orc):
 
 
 # ------------------------------------------------------------------ brute force
-@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["f32", "bf16", "fp8"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("S,T,G", [(1, 1, 1), (3, 5, 2), (5, 3, 1), (8, 8, 2), (4, 7, 3)])
 def test_brute_force_prefill(orc, kind, causal, S, T, G):
@@ -113,6 +113,10 @@ def test_brute_force_prefill(orc, kind, causal, S, T, G):
     case = gen.prefill_inputs(B, Hkv * G, Hkv, S, T, D, kind=kind, seed=100 + S * 7 + T)
     o, lse = orc.prefill(case, causal=causal)
     Q, K, V = (brute.decode_elems(case[n]) for n in "qkv")
+    if kind == "fp8":  # e4m3 bytes times their per-head scales
+        Q = Q * case["q_scale"].astype(np.float64)[None, None, :, None]
+        K = K * case["k_scale"].astype(np.float64)[None, None, :, None]
+        V = V * case["v_scale"].astype(np.float64)[None, None, :, None]
     ob, lb = brute.attention(Q, K, V, causal=causal, scale=case["scale"])
     np.testing.assert_allclose(o, ob, rtol=1e-12, atol=1e-12)
     np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(lb))
@@ -183,6 +187,20 @@ def test_int4_codes_decode_to_twos_complement_nibbles(orc):
     o2, _ = orc.attention(q, kbytes, vbytes, B=1, Hq=1, Hkv=1, S=1, T=0, D=D, causal=False, scale=0.125, layout=1,
                           k_scale=ones, v_scale=sc, page_size=T, kv_lens=np.array([T]), kv_kind="int4")
     np.testing.assert_allclose(o2[0, 0, 0], expect * np.repeat([1.0, 2.0], 32), rtol=0, atol=1e-12)
+
+
+def test_fp8_prefill_inputs_follow_per_head_scales():
+    """Each head's largest |value| maps to e4m3's largest finite value (448) and
+    every decoded value is within half an e4m3 step of the drawn one."""
+    case = gen.prefill_inputs(2, 4, 2, 16, 16, 64, kind="fp8", seed=5)
+    x = gen.normal((2, 16, 4, 64), 5, gen.TID_Q, "f32")
+    dec = brute.decode_elems(case["q"])
+    np.testing.assert_allclose(np.max(np.abs(dec), axis=(0, 1, 3)), 448.0)
+    back = dec * case["q_scale"][None, None, :, None]
+    # e4m3 has 3 mantissa bits: |error| <= 2^-4 |x| for normal values, and
+    # <= 2^-10 * scale in the subnormal range
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, case["q_scale"][None, None, :, None] * 2.0 ** -10)
+    assert np.all(np.abs(back - x) <= bound * (1 + 1e-9))
 
 
 def test_int4_quantizer_roundtrip():

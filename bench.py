@@ -8,6 +8,7 @@ only unmasked (query, key) pairs at 4*D flop each.  Beside it, in the same run:
     D=128, 512-token pages, ragged lengths U[1024, 32768]) in GB/s of KV bytes
     of valid tokens (+ q, o, lse), with the cache copies rotated so each
     timed launch streams from HBM rather than from the 256 MB last-level cache;
+  * ``prefill_fp8``: the same prefill with e4m3 Q/K/V and per-head scales;
   * ``decode_quant``: the same decode over contiguous int8, OCP e4m3fn and
     int4 caches (B=4, Hq=32, Hkv=8, D=128, T=65536) in GB/s of cache bytes;
   * ``decode_multi``: multi-token decode (n_q=4 verified tokens per sequence)
@@ -38,6 +39,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention TFLOP/s (prefill) + decode KV GB/s, as fraction of MI355X peak"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk (dense, published 2.5 PF)
+PEAK_FP8_TFLOPS = 5033.2  # dense fp8 matrix-core peak (published 5.0 PF)
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "exact_long_context_tiled_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -129,6 +131,44 @@ def bench_prefill(args):
     tflops = flops / (ms * 1e-3) / 1e12
     log(f"prefill: {ms:.4f} ms/launch, {tflops:.1f} TFLOP/s ({flops:.4e} flop)")
     return case, w, ms, flops, tflops
+
+
+def bench_prefill_fp8(args):
+    """The LLaMa-13B-shaped causal prefill with e4m3 Q/K/V and per-head scales
+    (codes drawn on the device).  Q.K^T runs on fp8 matrix cores and P.V on
+    bf16 ones, so the roofline peak is the blend of the two for equal flops."""
+    import torch
+
+    import attn_inputs as gen
+    import exact_long_context_tiled_amd as attn
+
+    w = gen.WORKLOADS["llama13b_gqa_causal_bf16"]
+    B, Hq, Hkv, S, T, D = w["B"], w["Hq"], w["Hkv"], w["S"], w["T"], w["D"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0x5EED + 8)
+    q = torch.randn((B, S, Hq, D), generator=g, device="cuda").mul_(64).to(torch.float8_e4m3fn)
+    k = torch.randn((B, T, Hkv, D), generator=g, device="cuda").mul_(64).to(torch.float8_e4m3fn)
+    v = torch.randn((B, T, Hkv, D), generator=g, device="cuda").mul_(64).to(torch.float8_e4m3fn)
+    qs = torch.full((Hq,), 1 / 64, device="cuda")
+    ks = torch.full((Hkv,), 1 / 64, device="cuda")
+    vs = torch.full((Hkv,), 1 / 64, device="cuda")
+    o = torch.empty((B, S, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(_):
+        attn.prefill_fp8(q, k, v, qs, ks, vs, causal=True, scale=1 / math.sqrt(D), out=o, lse=lse)
+
+    ms = timed(step, args.steps, args.warmup, stream)
+    flops = 4.0 * D * B * Hq * causal_pairs(S, T)
+    tflops = flops / (ms * 1e-3) / 1e12
+    peak = 1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS)
+    log(f"prefill fp8: {ms:.4f} ms/launch, {tflops:.1f} TFLOP/s")
+    return {"workload": "llama13b_gqa_causal_fp8", "value": round(tflops, 2), "unit": "TFLOP/s",
+            "ms_per_launch": round(ms, 5), "dtype": "e4m3 Q.K^T, bf16 P.V",
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+                         "frac": round(tflops / peak, 4), "traffic": None,
+                         "peak_note": "half the flops at the fp8 peak (5.0 PF), half at the bf16 peak (2.5 PF)"}}
 
 
 def bench_decode(args):
@@ -435,6 +475,7 @@ def main():
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": recorded_traffic("prefill_llama13b_pmc_traffic.md", "prefill_bf16.hip")},
     }
+    out["prefill_fp8"] = bench_prefill_fp8(args)
     if not args.no_decode:
         out["decode"] = bench_decode(args)
         out["decode_quant"] = bench_decode_quant(args)

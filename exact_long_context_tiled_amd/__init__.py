@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     lib_path,
     merge_partials,
     prefill,
+    prefill_fp8,
     stream_budgeted,
     stream_cqs,
     stream_cqs_plan,
@@ -30,7 +31,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "AttnError", "prefill", "decode_splitkv", "decode_workspace_size", "decode_multi",
+    "AttnError", "prefill", "prefill_fp8", "decode_splitkv", "decode_workspace_size", "decode_multi",
     "decode_multi_workspace_size", "merge_partials", "stream_budgeted",
     "stream_plan", "stream_cqs", "stream_cqs_plan", "last_error", "lib", "lib_path",
 ]

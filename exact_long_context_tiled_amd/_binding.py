@@ -55,6 +55,8 @@ def lib():
         P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
         L.attn_prefill.argtypes = [I, P, P, P, I, I, I, I64, I64, I, I, F, P, P, P]
         L.attn_prefill.restype = I
+        L.attn_prefill_fp8.argtypes = [P, P, P, P, P, P, I, I, I, I64, I64, I, I, F, P, P, P]
+        L.attn_prefill_fp8.restype = I
         L.attn_decode_workspace_size.argtypes = [I, I, I, I, I, I]
         L.attn_decode_workspace_size.restype = SZ
         L.attn_decode_splitkv.argtypes = [I, P, P, P, P, P, P, I, I, I, P, I, I, I, I, I, F, I, P, SZ, P, P, P]
@@ -127,6 +129,26 @@ def prefill(q, k, v, *, causal=True, scale=None, out=None, lse=None, return_lse=
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
     _check(lib().attn_prefill(_dt(q), _ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, S, T, D, int(causal), scale,
                               _ptr(out), _ptr(lse), _stream()))
+    return out, lse
+
+
+def prefill_fp8(q, k, v, q_scale, k_scale, v_scale, *, causal=True, scale=None, out=None, lse=None,
+                return_lse=True):
+    """fp8 prefill.  q [B,S,Hq,D], k/v [B,T,Hkv,D] float8_e4m3fn (or uint8 bytes)
+    device tensors; q_scale [Hq], k_scale / v_scale [Hkv] fp32 device tensors.
+    Returns (o [B,S,Hq,D] fp32, lse [B,Hq,S] fp32 or None)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (q_scale, "q_scale"), (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _need(t, n)
+    B, S, Hq, D = q.shape
+    T, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, S, Hq, D), dtype=torch.float32, device=q.device)
+    if lse is None and return_lse:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    _check(lib().attn_prefill_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), B, Hq,
+                                  Hkv, S, T, D, int(causal), scale, _ptr(out), _ptr(lse), _stream()))
     return out, lse
 
 

@@ -46,20 +46,28 @@ using namespace attn;
 
 extern "C" const char* attn_last_error(void) { return g_err; }
 
-extern "C" attn_status attn_prefill(attn_dtype dt, const void* q, const void* k, const void* v, int B, int Hq,
-                                    int Hkv, int64_t S, int64_t T, int D, int causal, float scale, float* o,
-                                    float* lse, void* stream) {
-  if (dt != ATTN_BF16 && dt != ATTN_F32)
-    return set_error(ATTN_E_UNSUPPORTED, "prefill: dtype must be ATTN_BF16 or ATTN_F32 (got %d)", (int)dt);
-  if (D != 64 && D != 128) return set_error(ATTN_E_UNSUPPORTED, "prefill: D must be 64 or 128 (got %d)", D);
+namespace {
+
+// Arguments of a whole-sequence prefill ([B, S, Hq, D] queries against
+// [B, T, Hkv, D] keys); validation shared by the bf16 / fp32 and fp8 calls.
+attn_status prefill_args(const char* what, const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                         int64_t S, int64_t T, int D, int causal, float scale, float* o, float* lse, PrefillArgs* out,
+                         bool* nothing) {
+  *nothing = false;
+  if (D != 64 && D != 128) return set_error(ATTN_E_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", what, D);
   if (B < 0 || S < 0 || T < 0 || Hq <= 0 || Hkv <= 0)
-    return set_error(ATTN_E_INVALID, "prefill: negative or zero sizes (B=%d Hq=%d Hkv=%d S=%lld T=%lld)", B, Hq,
+    return set_error(ATTN_E_INVALID, "%s: negative or zero sizes (B=%d Hq=%d Hkv=%d S=%lld T=%lld)", what, B, Hq,
                      Hkv, (long long)S, (long long)T);
-  if (Hq % Hkv) return set_error(ATTN_E_INVALID, "prefill: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
-  if (causal != 0 && causal != 1) return set_error(ATTN_E_INVALID, "prefill: causal must be 0 or 1");
-  if (!isfinite(scale)) return set_error(ATTN_E_INVALID, "prefill: scale must be finite");
-  if (B == 0 || S == 0) return ATTN_OK;
-  if (!q || !o || (T > 0 && (!k || !v))) return set_error(ATTN_E_INVALID, "prefill: null device pointer");
+  if (Hq % Hkv) return set_error(ATTN_E_INVALID, "%s: Hq=%d is not a multiple of Hkv=%d", what, Hq, Hkv);
+  if (causal != 0 && causal != 1) return set_error(ATTN_E_INVALID, "%s: causal must be 0 or 1", what);
+  // the kernels scale the row max of the raw scores, which needs scale > 0
+  if (!isfinite(scale) || !(scale > 0.f)) return set_error(ATTN_E_INVALID, "%s: scale must be finite and > 0", what);
+  if (B > 65535 || Hkv > 65535) return set_error(ATTN_E_UNSUPPORTED, "%s: B and Hkv must be <= 65535", what);
+  if (B == 0 || S == 0) {
+    *nothing = true;
+    return ATTN_OK;
+  }
+  if (!q || !o || (T > 0 && (!k || !v))) return set_error(ATTN_E_INVALID, "%s: null device pointer", what);
   PrefillArgs a{};
   a.q = q;
   a.k = T > 0 ? k : q;
@@ -85,9 +93,38 @@ extern "C" attn_status attn_prefill(attn_dtype dt, const void* q, const void* k,
   a.causal = causal;
   a.accumulate = 0;
   a.scale_log2 = scale * kLog2e;
-  if (B > 65535 || Hkv > 65535) return set_error(ATTN_E_UNSUPPORTED, "prefill: B and Hkv must be <= 65535");
+  *out = a;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" attn_status attn_prefill(attn_dtype dt, const void* q, const void* k, const void* v, int B, int Hq,
+                                    int Hkv, int64_t S, int64_t T, int D, int causal, float scale, float* o,
+                                    float* lse, void* stream) {
+  if (dt != ATTN_BF16 && dt != ATTN_F32)
+    return set_error(ATTN_E_UNSUPPORTED, "prefill: dtype must be ATTN_BF16 or ATTN_F32 (got %d)", (int)dt);
+  PrefillArgs a;
+  bool nothing;
+  attn_status st = prefill_args("prefill", q, k, v, B, Hq, Hkv, S, T, D, causal, scale, o, lse, &a, &nothing);
+  if (st != ATTN_OK || nothing) return st;
   return dt == ATTN_BF16 ? launch_prefill_bf16(a, D, (hipStream_t)stream)
                          : launch_prefill_f32(a, D, (hipStream_t)stream);
+}
+
+extern "C" attn_status attn_prefill_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                                        const float* k_scale, const float* v_scale, int B, int Hq, int Hkv,
+                                        int64_t S, int64_t T, int D, int causal, float scale, float* o, float* lse,
+                                        void* stream) {
+  PrefillArgs a;
+  bool nothing;
+  attn_status st = prefill_args("prefill_fp8", q, k, v, B, Hq, Hkv, S, T, D, causal, scale, o, lse, &a, &nothing);
+  if (st != ATTN_OK || nothing) return st;
+  if (!q_scale || !k_scale || !v_scale) return set_error(ATTN_E_INVALID, "prefill_fp8: null scale pointer");
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  return launch_prefill_fp8(a, D, (hipStream_t)stream);
 }
 
 namespace {
@@ -116,7 +153,7 @@ attn_status decode_impl(attn_dtype kv_dt, const void* q, const void* k_cache, co
   if (Hq % Hkv) return set_error(ATTN_E_INVALID, "decode: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   const int G = Hq / Hkv;
   if (G > 8) return set_error(ATTN_E_UNSUPPORTED, "decode: at most 8 query heads per KV head (got %d)", G);
-  if (!isfinite(scale)) return set_error(ATTN_E_INVALID, "decode: scale must be finite");
+  if (!isfinite(scale) || !(scale > 0.f)) return set_error(ATTN_E_INVALID, "decode: scale must be finite and > 0");
   if (num_splits > kDecodeMaxUnits)
     return set_error(ATTN_E_UNSUPPORTED, "decode: at most %d work units (got %d)", kDecodeMaxUnits, num_splits);
   if (B > 4095) return set_error(ATTN_E_UNSUPPORTED, "decode: at most 4095 sequences per call (got %d)", B);

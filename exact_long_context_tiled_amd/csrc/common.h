@@ -49,11 +49,16 @@ struct PrefillArgs {
   int causal;
   int accumulate;
   float scale_log2;  // scale * log2(e)
+  // e4m3 operands only: per-head scales, q [Hq], k and v [Hkv] (fp32, > 0)
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
 };
 
 // Launchers: validate nothing (the ABI layer did), launch on `stream`.
 attn_status launch_prefill_bf16(const PrefillArgs& a, int D, hipStream_t stream);
 attn_status launch_prefill_f32(const PrefillArgs& a, int D, hipStream_t stream);
+attn_status launch_prefill_fp8(const PrefillArgs& a, int D, hipStream_t stream);
 
 // ---------------------------------------------------------------- decode
 // The KV of the whole batch is one run of 16-token groups, segment by

@@ -279,7 +279,7 @@ extern "C" attn_status attn_stream_budgeted(attn_dtype dt, const void* q_host, c
   attn_status st = streamx::check_stream_sizes(dt, B, Hq, Hkv, S, T, D);
   if (st != ATTN_OK) return st;
   if (block_q < 0 || block_k < 0) return set_error(ATTN_E_INVALID, "stream: invalid sizes");
-  if (!std::isfinite(scale)) return set_error(ATTN_E_INVALID, "stream: scale must be finite");
+  if (!std::isfinite(scale) || !(scale > 0.f)) return set_error(ATTN_E_INVALID, "stream: scale must be finite and > 0");
   if (B == 0 || S == 0) {
     if (report) memset(report, 0, sizeof(*report));
     return ATTN_OK;

@@ -365,7 +365,8 @@ extern "C" attn_status attn_stream_cqs(attn_dtype dt, const void* q_host, const 
   attn_status st = streamx::check_stream_sizes(dt, B, Hq, Hkv, S, T, D);
   if (st != ATTN_OK) return st;
   if (n_blocks < 0) return set_error(ATTN_E_INVALID, "stream_cqs: invalid sizes");
-  if (!std::isfinite(scale)) return set_error(ATTN_E_INVALID, "stream_cqs: scale must be finite");
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return set_error(ATTN_E_INVALID, "stream_cqs: scale must be finite and > 0");
   if (B == 0 || S == 0) {
     if (info) memset(info, 0, sizeof(*info));
     if (report) memset(report, 0, sizeof(*report));

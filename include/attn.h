@@ -72,6 +72,7 @@ typedef enum attn_dtype {
  *   q       device, [B, S, Hq, D] of dt
  *   k, v    device, [B, T, Hkv, D] of dt
  *   causal  0 or 1 (bottom-right, see above)
+ *   scale   > 0 (the kernels scale each row's maximum raw score)
  *   o       device, [B, S, Hq, D] fp32 (written)
  *   lse     device, [B, Hq, S] fp32 (written), or NULL
  * Errors: ATTN_E_INVALID, ATTN_E_UNSUPPORTED (D, dt), ATTN_E_DEVICE.
@@ -79,6 +80,24 @@ typedef enum attn_dtype {
  */
 attn_status attn_prefill(attn_dtype dt, const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
                          int64_t S, int64_t T, int D, int causal, float scale, float* o, float* lse, void* stream);
+
+/*
+ * Tiled prefill with OCP e4m3fn (fp8) Q, K and V and per-head scales:
+ *   O = softmax(scale * (q_scale[h] q)(k_scale[hk] k)^T + mask) (v_scale[hk] v).
+ * Q.K^T runs on the fp8 matrix cores; the softmax weights are rounded to bf16
+ * for the P.V product (as in ATTN_BF16 prefill), with V's e4m3 values
+ * converted exactly to bf16.  (FP8 operands halving the bytes per token:
+ * LLM-CoOpt "Methodology" item 1; tiling and online softmax as attn_prefill.)
+ *
+ *   q        device, [B, S, Hq, D] e4m3fn bytes
+ *   k, v     device, [B, T, Hkv, D] e4m3fn bytes
+ *   q_scale  device fp32 [Hq]; k_scale, v_scale device fp32 [Hkv]; all > 0
+ *   other arguments as attn_prefill (scale > 0).
+ * Errors: ATTN_E_INVALID (incl. null scales), ATTN_E_UNSUPPORTED (D), ATTN_E_DEVICE.
+ */
+attn_status attn_prefill_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                             const float* k_scale, const float* v_scale, int B, int Hq, int Hkv, int64_t S,
+                             int64_t T, int D, int causal, float scale, float* o, float* lse, void* stream);
 
 /*
  * Workspace bytes attn_decode_splitkv needs for these sizes (num_splits as

@@ -25,7 +25,8 @@ def test_library_exports_every_declared_symbol():
     syms = _declared_symbols()
     assert set(syms) >= {"attn_prefill", "attn_decode_splitkv", "attn_merge_partials", "attn_stream_budgeted",
                          "attn_stream_plan", "attn_decode_workspace_size", "attn_last_error", "attn_stream_cqs",
-                         "attn_stream_cqs_plan", "attn_decode_multi", "attn_decode_multi_workspace_size"}
+                         "attn_stream_cqs_plan", "attn_decode_multi", "attn_decode_multi_workspace_size",
+                         "attn_prefill_fp8"}
     for s in syms:
         assert hasattr(L, s), s
 
@@ -50,6 +51,23 @@ def test_prefill_validation_before_any_launch():
     # empty work is a no-op even with null pointers
     assert L.attn_prefill(1, None, None, None, 0, 4, 2, 8, 8, 64, 1, 0.1, None, None, None) == 0
     assert L.attn_prefill(1, None, None, None, 2, 4, 2, 0, 8, 64, 1, 0.1, None, None, None) == 0
+    # the kernels scale each row's raw maximum: scale must be positive
+    assert L.attn_prefill(1, None, None, None, 1, 4, 2, 8, 8, 64, 1, 0.0, None, None, None) == 1
+    assert L.attn_prefill(1, None, None, None, 1, 4, 2, 8, 8, 64, 1, -0.5, None, None, None) == 1
+    assert "> 0" in attn.last_error()
+
+
+def test_prefill_fp8_validation_before_any_launch():
+    L = attn.lib()
+    f = L.attn_prefill_fp8
+    dummy = 256  # never dereferenced: validation fails or returns first
+    assert f(None, None, None, None, None, None, 1, 4, 2, 8, 8, 96, 1, 0.1, None, None, None) == 2  # D
+    assert f(None, None, None, None, None, None, 1, 5, 2, 8, 8, 64, 1, 0.1, None, None, None) == 1  # Hq % Hkv
+    assert f(None, None, None, None, None, None, 1, 4, 2, 8, 8, 64, 1, -1.0, None, None, None) == 1  # scale
+    assert f(None, None, None, None, None, None, 1, 4, 2, 8, 8, 64, 1, 0.1, None, None, None) == 1  # null q
+    assert f(dummy, dummy, dummy, None, dummy, dummy, 1, 4, 2, 8, 8, 64, 1, 0.1, dummy, None, None) == 1
+    assert "scale" in attn.last_error()
+    assert f(None, None, None, None, None, None, 0, 4, 2, 8, 8, 64, 1, 0.1, None, None, None) == 0  # no work
 
 
 def test_decode_and_merge_validation():

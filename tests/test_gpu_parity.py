@@ -98,6 +98,50 @@ def test_prefill_bf16_shapes(B, Hq, Hkv, S, T, D, causal):
     check_lp(o, lse, ro, rl, f"bf16 {B,Hq,Hkv,S,T,D,causal}")
 
 
+def gpu_prefill_fp8(case, causal=True):
+    q, k, v = (to_dev(case[n], "fp8") for n in "qkv")
+    qs, ks, vs = (to_dev(case[n + "_scale"]) for n in "qkv")
+    o, lse = attn.prefill_fp8(q, k, v, qs, ks, vs, causal=causal, scale=case["scale"])
+    torch.cuda.synchronize()
+    return o.cpu().numpy(), lse.cpu().numpy()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,T,D,causal", BF16_SHAPES)
+def test_prefill_fp8_shapes(B, Hq, Hkv, S, T, D, causal):
+    """e4m3 Q/K/V with per-head scales == oracle on the same bytes and scales."""
+    import oracle
+    case = gen.prefill_inputs(B, Hq, Hkv, S, T, D, kind="fp8", seed=13 + S * 3 + T)
+    say(f"fp8 prefill {B,Hq,Hkv,S,T,D,causal}")
+    o, lse = gpu_prefill_fp8(case, causal)
+    ro, rl = oracle.prefill(case, causal=causal)
+    if causal and S > T:
+        dead = S - T
+        assert np.all(o[:, :dead] == 0) and np.all(np.isneginf(lse[:, :, :dead]))
+    check_lp(o, lse, ro, rl, f"fp8 {B,Hq,Hkv,S,T,D,causal}")
+
+
+def test_prefill_fp8_llama13b_sampled_rows():
+    """B=4 Hq=40 Hkv=8 S=T=4096 D=128 causal, e4m3 operands: 64 sampled rows x all heads vs the oracle."""
+    import oracle
+    w = gen.WORKLOADS["llama13b_gqa_causal_bf16"]
+    case = gen.prefill_inputs(w["B"], w["Hq"], w["Hkv"], w["S"], w["T"], w["D"], kind="fp8", seed=0x5EED + 8)
+    o, lse = gpu_prefill_fp8(case, True)
+    rows = gen.sample_rows(w["S"], 64, 0x5EED + 8)
+    ro, rl = oracle.prefill(case, causal=True, rows=rows)
+    check_lp(o[:, rows], lse[:, :, rows], ro, rl, "fp8 llama13b sampled rows")
+
+
+def test_prefill_fp8_empty_keys_and_errors():
+    case = gen.prefill_inputs(1, 4, 2, 10, 0, 128, kind="fp8", seed=5)
+    o, lse = gpu_prefill_fp8(case, True)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+    q = to_dev(case["q"], "fp8")
+    qs = to_dev(case["q_scale"])
+    with pytest.raises(attn.AttnError) as e:
+        attn.prefill_fp8(q, q, q, qs, qs, qs, causal=True, scale=-1.0)
+    assert e.value.status == 1
+
+
 def test_prefill_empty_keys():
     case = gen.prefill_inputs(1, 4, 2, 10, 0, 128, kind="bf16", seed=5)
     o, lse = gpu_prefill(case, True)

@@ -79,6 +79,7 @@ struct DecodeArgs {
   const int32_t* kv_lens;
   int max_kv_len;  // lengths are clamped to [0, max_kv_len]
   int B, Hq, Hkv;
+  int G;        // Hq / Hkv
   int n_q;      // query tokens per sequence (rows of the segment: n_q * G)
   int n_units;  // N
   float scale_log2;
@@ -97,8 +98,12 @@ constexpr int kDecodeMaxUnits = 65535;
 __host__ __device__ inline int decode_record_floats(int rows, int D) { return rows * D + (rows + 15) / 16 * 16; }
 size_t decode_workspace_bytes(int B, int Hkv, int rows, int D, int n_units_bound);
 // n_units == 0 picks one work-group per compute unit (at most
-// kDecodeMaxAutoUnits); the merge kernel runs after the split kernel.
+// kDecodeMaxAutoUnits); the merge kernel runs after the split kernel.  The
+// split runs on the matrix cores for bf16 / e4m3 / int8 caches (unless
+// ATTN_DECODE_PATH=valu), on the vector ALUs otherwise.
 attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a, int D, int G, hipStream_t stream);
+bool decode_mfma_supported(attn_dtype kv_dt);
+attn_status launch_decode_split_mfma(attn_dtype kv_dt, const DecodeArgs& a, int D, hipStream_t stream);
 
 // ---------------------------------------------------------------- merge
 attn_status launch_merge(int n, const float* o_parts, const float* lse_parts, int64_t R, int D, float* o,

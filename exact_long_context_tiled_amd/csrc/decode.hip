@@ -42,12 +42,19 @@
 #include <math.h>
 #include <stdlib.h>
 
+#include <string.h>
+
 #include <algorithm>
 
 #include "common.h"
+#include "decode_common.h"
 
 namespace attn {
 namespace {
+
+using dec::clamp_len;
+using dec::group_prefix;
+using dec::lane_pair;
 
 // A lane's slice of a token's K or V row: 16 bytes (8 bf16, 16 e4m3 or 16
 // int8 elements) or, for int4, 8 bytes (16 packed elements, so that a lane
@@ -180,26 +187,6 @@ __device__ __forceinline__ void k_pairs(const typename KvTraits<KV>::Slice& raw,
   }
 }
 
-// {a, b} = {x of this lane, x of lane ^ OFF} in a lane-fixed order (the
-// combine below is symmetric in the two): one permlane swap for OFF = 32 or
-// 16, a row rotation for OFF = 8, an LDS-free bpermute otherwise.
-template <int OFF>
-__device__ __forceinline__ void lane_pair(float x, float& a, float& b) {
-  if constexpr (OFF == 32 || OFF == 16) {
-    const uint32_t u = __float_as_uint(x);
-    const auto r = OFF == 32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
-                             : __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-  } else if constexpr (OFF == 8) {
-    a = x;
-    b = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
-  } else {
-    a = x;
-    b = __shfl_xor(x, OFF);
-  }
-}
-
 // Merge the online-softmax states (m, l, acc) of lanes OFF apart.
 template <int OFF, int G, int EPL>
 __device__ __forceinline__ void combine_lanes(float (&m)[G], float (&l)[G], float (&acc)[G][EPL]) {
@@ -220,40 +207,6 @@ __device__ __forceinline__ void combine_lanes(float (&m)[G], float (&l)[G], floa
     }
     m[g] = M;
   }
-}
-
-__device__ __forceinline__ int clamp_len(int t, int max_len) { return min(max(t, 0), max_len); }
-
-// pre[b] = groups of all segments of sequences < b (per KV head), pre[B] = total;
-// computed by the whole work-group into LDS.
-template <int THREADS>
-__device__ void group_prefix(const int32_t* __restrict__ lens, int B, int max_len, int64_t* pre,
-                             int64_t* wsum) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int per = (B + THREADS - 1) / THREADS;
-  const int b0 = tid * per;
-  int64_t s = 0;
-  for (int k = 0; k < per; ++k)
-    if (b0 + k < B) s += (clamp_len(lens[b0 + k], max_len) + kDecodeGroup - 1) / kDecodeGroup;
-  int64_t x = s;  // inclusive scan over the wave
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int64_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) wsum[w] = x;
-  __syncthreads();
-  int64_t base = 0;
-  for (int ww = 0; ww < w; ++ww) base += wsum[ww];
-  int64_t run = base + x - s;
-  for (int k = 0; k < per; ++k) {
-    if (b0 + k < B) {
-      pre[b0 + k] = run;
-      run += (clamp_len(lens[b0 + k], max_len) + kDecodeGroup - 1) / kDecodeGroup;
-    }
-  }
-  if (tid == THREADS - 1) pre[B] = base + x;
-  __syncthreads();
 }
 
 constexpr int kDecodeWaves = 4;  // waves per work-group
@@ -666,19 +619,8 @@ attn_status launch_one(DecodeArgs a, hipStream_t stream) {
       return set_error(ATTN_E_DEVICE, "decode: cannot raise the LDS limit");
     lds_set = true;
   }
-  if (a.n_units <= 0) {
-    // one work-group per compute unit: measured faster than filling every
-    // resident slot (fewer partial records, and the scan stays bandwidth-bound)
-    a.n_units = std::min(kDecodeMaxAutoUnits, device_cu_count());
-    const char* env = getenv("ATTN_DECODE_UNITS");
-    if (env && atoi(env) > 0) a.n_units = std::min(kDecodeMaxAutoUnits, atoi(env));
-  }
   hipLaunchKernelGGL(kern, dim3(a.n_units), dim3(kDecodeThreads), lds, stream, a);
-  attn_status st = check_launch("decode_split");
-  if (st != ATTN_OK) return st;
-  const int64_t rows = (int64_t)a.B * a.n_q * a.Hq;
-  hipLaunchKernelGGL(decode_merge_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a, G);
-  return check_launch("decode_merge");
+  return check_launch("decode_split");
 }
 
 // Query tokens per row chunk: enough to cover n_q in as few chunks as the
@@ -727,15 +669,37 @@ size_t decode_workspace_bytes(int B, int Hkv, int rows, int D, int n_units_bound
   return rec_bytes + (segs * 2 * sizeof(int32_t) + 255) / 256 * 256;
 }
 
-attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a, int D, int G, hipStream_t stream) {
-  switch (kv_dt) {
-    case ATTN_BF16: return launch_d<ATTN_BF16>(a, D, G, stream);
-    case ATTN_FP8_E4M3: return launch_d<ATTN_FP8_E4M3>(a, D, G, stream);
-    case ATTN_INT8: return launch_d<ATTN_INT8>(a, D, G, stream);
-    case ATTN_INT4: return launch_d<ATTN_INT4>(a, D, G, stream);
-    default: break;
+attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a0, int D, int G, hipStream_t stream) {
+  DecodeArgs a = a0;
+  a.G = G;
+  if (a.n_units <= 0) {
+    // one work-group per compute unit: measured faster than filling every
+    // resident slot (fewer partial records, and the scan stays bandwidth-bound)
+    a.n_units = std::min(kDecodeMaxAutoUnits, device_cu_count());
+    const char* env = getenv("ATTN_DECODE_UNITS");
+    if (env && atoi(env) > 0) a.n_units = std::min(kDecodeMaxAutoUnits, atoi(env));
   }
-  return set_error(ATTN_E_UNSUPPORTED, "decode: unsupported KV dtype %d", (int)kv_dt);
+  const char* path = getenv("ATTN_DECODE_PATH");
+  const bool valu = path && strcmp(path, "valu") == 0;
+  attn_status st;
+  if (decode_mfma_supported(kv_dt) && !valu) {
+    st = launch_decode_split_mfma(kv_dt, a, D, stream);
+  } else {
+    switch (kv_dt) {
+      case ATTN_BF16: st = launch_d<ATTN_BF16>(a, D, G, stream); break;
+      case ATTN_FP8_E4M3: st = launch_d<ATTN_FP8_E4M3>(a, D, G, stream); break;
+      case ATTN_INT8: st = launch_d<ATTN_INT8>(a, D, G, stream); break;
+      case ATTN_INT4: st = launch_d<ATTN_INT4>(a, D, G, stream); break;
+      default: return set_error(ATTN_E_UNSUPPORTED, "decode: unsupported KV dtype %d", (int)kv_dt);
+    }
+  }
+  if (st != ATTN_OK) return st;
+  const int64_t rows = (int64_t)a.B * a.n_q * a.Hq;
+  if (D == 128)
+    hipLaunchKernelGGL(decode_merge_kernel<128>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a, G);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<64>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a, G);
+  return check_launch("decode_merge");
 }
 
 }  // namespace attn

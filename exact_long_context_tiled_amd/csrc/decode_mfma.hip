@@ -1,0 +1,506 @@
+// Split-KV decode on the matrix cores (bf16, e4m3 and int8 caches).
+//
+// The work split, the partial records and the log-sum-exp merge are those of
+// the vector-ALU kernel in decode.hip (flash decoding: ONNX Runtime PR #28695
+// analysis, section 2; pages: LLM-CoOpt "Methodology" item 3; quantised
+// caches dequantised on the fly: LLM-CoOpt "Methodology" item 1 and the
+// ONNX Runtime analysis, section 1).  Only the scan of a piece differs: the
+// query rows of a KV head (n_q * G of them, up to 16 per pass) form the
+// n = 16 side of v_mfma_f32_16x16x32_bf16 products, so the per-token work
+// moves from the vector ALUs to the matrix cores:
+//
+//   S^T = K Q^T   (16 tokens x 16 rows per product).  K comes straight from
+//                 HBM into the A operand: a lane quarter j holds D/4
+//                 contiguous dims of a token row (one to four 16-byte loads),
+//                 Q the same dims of its row.  The 16 tokens of sub-block sb
+//                 of a 32-token block are taken in the order
+//                 8*(i/4) + 4*sb + i%4 (i = A row), which makes the
+//                 accumulator of lane quarter j hold tokens 8j .. 8j+7 of the
+//                 block: the B operand of the next product as it stands.
+//   O^T += V^T P^T (16 dims x 16 rows, 32 tokens per product).  V goes
+//                 through LDS (direct global -> LDS copies into a per-wave
+//                 double buffer) and comes back transposed: two 16-bit
+//                 transposing reads (4 tokens each) for bf16, one 8-bit read
+//                 (8 tokens) for e4m3 / int8, converted exactly to bf16.
+//
+// e4m3 and int8 codes become exact bf16 numbers; P is rounded to bf16 as in
+// the prefill kernels.  int8 scales (per token) multiply the fp32 scores and
+// the softmax weights; e4m3 scales (per KV head) join scale*log2(e) and the
+// output factor.  Each of the 4 waves of a work-group scans every 4th
+// 32-token block of a piece with its own online softmax; the waves are then
+// combined through LDS and the piece's record (or the final output) written.
+#include <math.h>
+#include <stdlib.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "decode_common.h"
+
+namespace attn {
+namespace {
+
+using dec::clamp_len;
+using dec::group_prefix;
+using dec::lane_pair;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBlk = 32;   // tokens per wave iteration
+constexpr int kRows = 16;  // query rows per pass (the products' n)
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(int)))) int i32x2;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void copy16_to_lds(const void* src, lds_void* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int KV>
+constexpr int elem_bytes() {
+  return KV == ATTN_BF16 ? 2 : 1;
+}
+
+// Eight 8-bit codes (two words, element order) -> eight exact bf16 values.
+template <int KV>
+__device__ __forceinline__ bf16x8 codes8_to_bf16(uint32_t w0, uint32_t w1) {
+  if constexpr (KV == ATTN_FP8_E4M3) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  } else {
+    // int8 -> fp32 (exact), whose upper half is the exact bf16
+    const uint32_t w[2] = {w0, w1};
+    uint32_t pk[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const uint32_t src = w[h >> 1];
+      const int sh = 16 * (h & 1);
+      const float f0 = (float)(int)(int8_t)(src >> sh);
+      const float f1 = (float)(int)(int8_t)(src >> (sh + 8));
+      pk[h] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+    }
+    return __builtin_bit_cast(bf16x8, uint4{pk[0], pk[1], pk[2], pk[3]});
+  }
+}
+
+template <int KV, int D>
+struct MTile {
+  static constexpr int EB = elem_bytes<KV>();
+  static constexpr int ROWB = D * EB;                 // bytes per token row
+  static constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+  static constexpr int BYTES = kBlk * ROWB;           // one wave's V tile
+  static constexpr int COPIES = BYTES / 1024;         // wave-wide 1 KiB copies per tile
+  static constexpr int QD = D / 4;                    // dims per lane quarter (QK operands)
+  static constexpr int KL = QD * EB / 16;             // 16-byte K loads per token per lane
+  static constexpr int NKS = D / 32;                  // k-steps of the QK product
+  static constexpr int NDB = D / 16;                  // 16-dim blocks of the PV product
+  // V tiles of all waves, later overlaid by the wave partials of the combine
+  static constexpr int TILES = kWaves * 2 * BYTES;
+  static constexpr int RED = (kWaves * kRows * D + 2 * kWaves * kRows) * 4;
+  static constexpr int REGION = (TILES > RED ? TILES : RED + 255) / 256 * 256;
+};
+
+// V tile swizzle (16-byte chunk c of row r sits at c ^ swz(r)), chosen so the
+// transposing reads of a 16-lane group touch distinct banks.
+template <int KV, int D>
+__device__ __forceinline__ int swz_v(int r) {
+  using TL = MTile<KV, D>;
+  if constexpr (KV == ATTN_BF16) return (2 * (r & 3)) & (TL::CPR - 1);
+  else return r & (TL::CPR - 1);
+}
+
+template <int KV, int D>
+__global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
+  using TL = MTile<KV, D>;
+  constexpr int EB = TL::EB;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  char* vtiles = smem;                                     // [waves][2][BYTES]
+  int64_t* pre = (int64_t*)(smem + TL::REGION);            // [B + 1]
+  __shared__ int64_t wsum[kWaves];
+  // wave partials for the combine, overlaid on the V tiles once a pass is done
+  float* red_acc = (float*)smem;                           // [waves][kRows][D]
+  float* red_m = red_acc + kWaves * kRows * D;             // [waves][kRows]
+  float* red_l = red_m + kWaves * kRows;                   // [waves][kRows]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane >> 4, i = lane & 15;  // lane quarter, lane in quarter
+  const uint8_t* kb = (const uint8_t*)a.k;
+  const uint8_t* vb = (const uint8_t*)a.v;
+  char* vt0 = vtiles + (2 * w) * TL::BYTES;
+  char* vt1 = vt0 + TL::BYTES;
+
+  group_prefix<kThreads>(a.kv_lens, a.B, a.max_kv_len, pre, wsum);
+  const int64_t W = pre[a.B] * a.Hkv;
+  const int64_t N = a.n_units < W ? (int64_t)a.n_units : W;
+  const int unit = blockIdx.x;
+  if (unit >= N) return;
+  const int64_t x1 = (unit + 1) * W / N;
+  const int G = a.G;
+  const int n_q = a.n_q;
+  const int RT = n_q * G;
+  const int REC = decode_record_floats(RT, D);
+
+  for (int64_t pos = unit * W / N; pos < x1;) {
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] * a.Hkv <= pos) lo = mid;
+      else hi = mid - 1;
+    }
+    const int b = __builtin_amdgcn_readfirstlane(lo);
+    const int64_t sbase = pre[b] * a.Hkv;
+    const int ng = (int)(pre[b + 1] - pre[b]);
+    const int hk = __builtin_amdgcn_readfirstlane((int)((pos - sbase) / ng));
+    const int j0 = (int)(pos - sbase - (int64_t)hk * ng);
+    const int64_t seg_end = sbase + (int64_t)(hk + 1) * ng;
+    const int64_t pend = seg_end < x1 ? seg_end : x1;
+    const int T = clamp_len(a.kv_lens[b], a.max_kv_len);
+    const int t0 = __builtin_amdgcn_readfirstlane(j0 * kDecodeGroup);
+    const int t1 = __builtin_amdgcn_readfirstlane(min(T, (j0 + (int)(pend - pos)) * kDecodeGroup));
+    const int seg = b * a.Hkv + hk;
+    const bool whole = j0 == 0 && pend == seg_end;
+    float smul = a.scale_log2;
+    if constexpr (KV == ATTN_FP8_E4M3) smul *= a.k_scale[hk];
+    const int64_t hk_rows = (int64_t)hk * a.page_size;
+    float* rec = a.part + (int64_t)(unit + seg) * REC;
+
+    for (int r0 = 0; r0 < RT; r0 += kRows) {
+      const int n_rows = min(kRows, RT - r0);
+      // this lane's row (clamped onto the pass's last row when past it: computed, not written)
+      const int r = r0 + min(i, n_rows - 1);
+      const int sq = r / G, g = r - (r / G) * G;
+      // query token sq sits at T - n_q + sq and sees the keys before T - (n_q - 1 - sq)
+      const int lim = max(t0, min(t1, T - (n_q - 1 - sq)));
+      const int tend = __builtin_amdgcn_readfirstlane(
+          max(t0, min(t1, T - (n_q - 1 - (r0 + n_rows - 1) / G))));  // past the last key any row reads
+
+      // Q operand: dims QD*j .. of the lane's row
+      bf16x8 qf[TL::NKS];
+      {
+        const bf16x8* qp = (const bf16x8*)((const uint16_t*)a.q +
+                                           (((int64_t)b * n_q + sq) * a.Hq + (int64_t)hk * G + g) * D + TL::QD * j);
+#pragma unroll
+        for (int ks = 0; ks < TL::NKS; ++ks) qf[ks] = qp[ks];
+      }
+      f32x4 acc[TL::NDB];
+#pragma unroll
+      for (int db = 0; db < TL::NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      float m = -INFINITY, l = 0.f;
+
+      // cache row (token row index) of token t < tend of this segment
+      auto page_row = [&](int t16) {  // first row of the 16-token group holding token t16 (wave-uniform)
+        if (a.page_table) {
+          const auto* pt = (const __attribute__((address_space(4))) int32_t*)a.page_table;
+          const int pg = pt[(int64_t)b * a.max_pages + (t16 >> a.page_shift)];
+          return (int64_t)pg * a.Hkv * a.page_size + hk_rows - (t16 & ~(a.page_size - 1));
+        }
+        return (int64_t)b * a.Hkv * a.page_size + hk_rows;
+      };
+      struct Kbuf {
+        uint4 k[2][TL::KL];
+        float4 ks[2], vs[2];  // int8: scales of tokens 8j .. 8j+7 of the block
+      };
+      // loads of block starting at token g0: K operands to registers, V tile to LDS
+      auto issue = [&](int g0, Kbuf& kbf, char* vt) {
+        const int tl = tend - 1;
+        const int64_t base0 = page_row(__builtin_amdgcn_readfirstlane(min(g0, tl)));
+        const int64_t base1 = page_row(__builtin_amdgcn_readfirstlane(min(g0 + 16, tl)));
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const int tk = min(g0 + 8 * (i >> 2) + 4 * sb + (i & 3), tl);
+          const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
+          const uint4* src = (const uint4*)(kb + row * TL::ROWB + TL::QD * EB * j);
+#pragma unroll
+          for (int u = 0; u < TL::KL; ++u) kbf.k[sb][u] = src[u];
+        }
+        if constexpr (KV == ATTN_INT8) {
+          // the per-token scales of this lane quarter's 8 tokens (one 8-token run
+          // inside a page): two 16-byte loads each, or clamped single loads at the end
+          const int tb = g0 + 8 * j;
+          const int64_t base = (tb - g0 < 16 ? base0 : base1);
+          if (tb + 8 <= tend && ((base + tb) & 3) == 0) {  // (16-byte aligned runs)
+            const float4* kp = (const float4*)(a.k_scale + base + tb);
+            const float4* vp = (const float4*)(a.v_scale + base + tb);
+            kbf.ks[0] = kp[0];
+            kbf.ks[1] = kp[1];
+            kbf.vs[0] = vp[0];
+            kbf.vs[1] = vp[1];
+          } else {
+            float kk[8], vv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int tk = min(tb + e, tl);
+              const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
+              kk[e] = a.k_scale[row];
+              vv[e] = a.v_scale[row];
+            }
+            kbf.ks[0] = float4{kk[0], kk[1], kk[2], kk[3]};
+            kbf.ks[1] = float4{kk[4], kk[5], kk[6], kk[7]};
+            kbf.vs[0] = float4{vv[0], vv[1], vv[2], vv[3]};
+            kbf.vs[1] = float4{vv[4], vv[5], vv[6], vv[7]};
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < TL::COPIES; ++c) {
+          const int off = c * 1024 + 16 * lane;
+          const int rr = off / TL::ROWB;
+          const int pch = (off % TL::ROWB) / 16;
+          const int tk = min(g0 + rr, tl);
+          const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
+          copy16_to_lds(vb + row * TL::ROWB + 16 * (pch ^ swz_v<KV, D>(rr)), (lds_void*)(vt + c * 1024));
+        }
+      };
+      // V^T operands of a block: lane (j, i) holds dim 16*db + i of tokens 8j .. 8j+7
+      struct Vops {
+        bf16x8 v[TL::NDB];
+      };
+      auto vread = [&](const char* vt, Vops& vo) {
+        bf16x8* vop = vo.v;
+        if constexpr (KV == ATTN_BF16) {
+#pragma unroll
+          for (int db = 0; db < TL::NDB; ++db) {
+            const int col = 32 * db + 8 * (i & 3);  // byte within the row
+            const int r_lo = 8 * j + (i >> 2), r_hi = r_lo + 4;
+            const char* p0 = vt + r_lo * TL::ROWB + 16 * ((col >> 4) ^ swz_v<KV, D>(r_lo)) + (col & 15);
+            const char* p1 = vt + r_hi * TL::ROWB + 16 * ((col >> 4) ^ swz_v<KV, D>(r_hi)) + (col & 15);
+            const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+            const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+            vop[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        } else {
+          i32x2 raw[TL::NDB];
+#pragma unroll
+          for (int db = 0; db < TL::NDB; ++db) {
+            const int rrow = 8 * j + (i >> 1);
+            const char* p = vt + rrow * TL::ROWB + 16 * (db ^ swz_v<KV, D>(rrow)) + 8 * (i & 1);
+            raw[db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
+          }
+#pragma unroll
+          for (int db = 0; db < TL::NDB; ++db) vop[db] = codes8_to_bf16<KV>((uint32_t)raw[db][0], (uint32_t)raw[db][1]);
+        }
+      };
+      auto consume = [&](int g0, const Kbuf& kbf, const Vops& vo) {
+        const bf16x8* vop = vo.v;
+        // S^T = K Q^T for the two 16-token sub-blocks
+        f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+          for (int ks = 0; ks < TL::NKS; ++ks) {
+            bf16x8 kop;
+            if constexpr (KV == ATTN_BF16) {
+              kop = __builtin_bit_cast(bf16x8, kbf.k[sb][ks]);
+            } else {
+              const uint4 wv = kbf.k[sb][ks >> 1];
+              kop = (ks & 1) ? codes8_to_bf16<KV>(wv.z, wv.w) : codes8_to_bf16<KV>(wv.x, wv.y);
+            }
+            s[sb] = mfma16(kop, qf[ks], s[sb]);
+          }
+        }
+        // scores of tokens 8j + e of the block (e = 4*sb + register), this lane's row
+        float sc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[e] = s[e >> 2][e & 3];
+        float vsc[8];
+        if constexpr (KV == ATTN_INT8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            sc[e] *= kbf.ks[e >> 2][e & 3];
+            vsc[e] = kbf.vs[e >> 2][e & 3];
+          }
+        }
+        if (g0 + kBlk > lim) {  // keys past this row's limit weigh nothing
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc[e] = g0 + 8 * j + e < lim ? sc[e] : -INFINITY;
+        }
+        float mx = sc[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+        {
+          float u0, u1;
+          lane_pair<16>(mx, u0, u1);
+          mx = fmaxf(u0, u1);
+          lane_pair<32>(mx, u0, u1);
+          mx = fmaxf(u0, u1);
+        }
+        const float tx = mx * smul;
+        if (__builtin_amdgcn_ballot_w64(tx > m + 8.f) != 0) {
+          const float m_new = fmaxf(m, tx);
+          const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+          m = m_new;
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < TL::NDB; ++db) acc[db] *= alpha;
+        }
+        const float m_use = m == -INFINITY ? 0.f : m;
+        bf16x8 pf;
+        float ls = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float p = __builtin_amdgcn_exp2f(fmaf(sc[e], smul, -m_use));
+          ls += p;
+          if constexpr (KV == ATTN_INT8) p = sc[e] == -INFINITY ? 0.f : p * vsc[e];
+          pf[e] = (__bf16)p;
+        }
+        l += ls;
+        // O^T += V^T P^T
+#pragma unroll
+        for (int db = 0; db < TL::NDB; ++db) acc[db] = mfma16(vop[db], pf, acc[db]);
+      };
+
+      // two-stage pipeline over this wave's blocks (every 4th 32-token block
+      // of [t0, tend)); counted, with a single loop exit
+      const int nblk = tend > t0 ? (tend - t0 + kBlk - 1) / kBlk : 0;
+      const int n_it = nblk > w ? (nblk - w + kWaves - 1) / kWaves : 0;
+      constexpr int kStride = kWaves * kBlk;
+      int g0 = t0 + w * kBlk;
+      // (the transposing V reads of a block come before the next block's
+      // direct-to-LDS copies: issued while copies are in flight, they would
+      // make the compiler wait for those copies first)
+      if (n_it > 0) {
+        Kbuf k0, k1;
+        Vops vo;
+        issue(g0, k0, vt0);
+        int it = 0;
+        for (; it + 2 <= n_it; it += 2) {
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this block's loads have landed
+          vread(vt0, vo);
+          __builtin_amdgcn_sched_barrier(0);
+          issue(g0 + kStride, k1, vt1);
+          __builtin_amdgcn_sched_barrier(0);
+          consume(g0, k0, vo);
+          __builtin_amdgcn_s_waitcnt(0x0F70);
+          vread(vt1, vo);
+          __builtin_amdgcn_sched_barrier(0);
+          if (it + 2 < n_it) issue(g0 + 2 * kStride, k0, vt0);
+          __builtin_amdgcn_sched_barrier(0);
+          consume(g0 + kStride, k1, vo);
+          g0 += 2 * kStride;
+        }
+        if (it < n_it) {
+          __builtin_amdgcn_s_waitcnt(0x0F70);
+          vread(vt0, vo);
+          consume(g0, k0, vo);
+        }
+      }
+
+      // the row's sum over the lane quarters; then combine the waves through LDS
+      {
+        float u0, u1;
+        lane_pair<16>(l, u0, u1);
+        l = u0 + u1;
+        lane_pair<32>(l, u0, u1);
+        l = u0 + u1;
+      }
+      __syncthreads();  // every wave is done with its V tiles (the partials overlay them)
+#pragma unroll
+      for (int db = 0; db < TL::NDB; ++db)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) red_acc[(w * kRows + i) * D + 16 * db + 4 * j + q] = acc[db][q];
+      if (j == 0) {
+        red_m[w * kRows + i] = m;
+        red_l[w * kRows + i] = l;
+      }
+      __syncthreads();
+      float vmul = 1.f;
+      if constexpr (KV == ATTN_FP8_E4M3) vmul = a.v_scale[hk];
+      for (int idx = tid; idx < n_rows * D; idx += kThreads) {
+        const int rr = idx / D, d = idx - rr * D;
+        float M = red_m[rr];
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, red_m[ww * kRows + rr]);
+        float num = 0.f, den = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float mw = red_m[ww * kRows + rr];
+          const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+          num = fmaf(f, red_acc[(ww * kRows + rr) * D + d], num);
+          den = fmaf(f, red_l[ww * kRows + rr], den);
+        }
+        const float val = den > 0.f ? num * (vmul / den) : 0.f;
+        const int rg = r0 + rr;
+        if (whole) {
+          const int64_t orow = ((int64_t)b * n_q + rg / G) * a.Hq + (int64_t)hk * G + rg % G;
+          a.o[orow * D + d] = val;
+        } else {
+          rec[(int64_t)rg * D + d] = val;
+        }
+      }
+      if (tid < n_rows) {
+        float M = red_m[tid];
+#pragma unroll
+        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, red_m[ww * kRows + tid]);
+        float den = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float mw = red_m[ww * kRows + tid];
+          den = fmaf(mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M), red_l[ww * kRows + tid], den);
+        }
+        const float v = den > 0.f ? M + __log2f(den) : -INFINITY;
+        const int rg = r0 + tid;
+        if (!whole) rec[(int64_t)RT * D + rg] = v;
+        else if (a.lse) a.lse[((int64_t)b * a.Hq + (int64_t)hk * G + rg % G) * n_q + rg / G] = v * kLn2;
+      }
+      __syncthreads();  // the partials are read before the next pass's copies land
+    }
+    if (tid == 0 && j0 == 0) {
+      const int last = whole ? unit : (int)((seg_end * N - 1) / W);
+      a.seg_info[2 * seg] = unit + seg;
+      a.seg_info[2 * seg + 1] = last - unit + 1;
+    }
+    pos = pend;
+  }
+}
+
+template <int KV, int D>
+size_t mfma_lds_bytes(int B) {
+  return (size_t)MTile<KV, D>::REGION + (size_t)(B + 1) * sizeof(int64_t);
+}
+
+template <int KV, int D>
+attn_status launch_kd(const DecodeArgs& a, hipStream_t stream) {
+  auto kern = decode_mfma_kernel<KV, D>;
+  const size_t lds = mfma_lds_bytes<KV, D>(a.B);
+  static bool lds_set = false;
+  if (!lds_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)mfma_lds_bytes<KV, D>(4095)) != hipSuccess)
+      return set_error(ATTN_E_DEVICE, "decode: cannot raise the LDS limit");
+    lds_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(a.n_units), dim3(kThreads), lds, stream, a);
+  return check_launch("decode_mfma");
+}
+
+}  // namespace
+
+bool decode_mfma_supported(attn_dtype kv_dt) {
+  return kv_dt == ATTN_BF16 || kv_dt == ATTN_FP8_E4M3 || kv_dt == ATTN_INT8;
+}
+
+attn_status launch_decode_split_mfma(attn_dtype kv_dt, const DecodeArgs& a, int D, hipStream_t stream) {
+  switch (kv_dt) {
+    case ATTN_BF16: return D == 128 ? launch_kd<ATTN_BF16, 128>(a, stream) : launch_kd<ATTN_BF16, 64>(a, stream);
+    case ATTN_FP8_E4M3:
+      return D == 128 ? launch_kd<ATTN_FP8_E4M3, 128>(a, stream) : launch_kd<ATTN_FP8_E4M3, 64>(a, stream);
+    case ATTN_INT8: return D == 128 ? launch_kd<ATTN_INT8, 128>(a, stream) : launch_kd<ATTN_INT8, 64>(a, stream);
+    default: break;
+  }
+  return set_error(ATTN_E_UNSUPPORTED, "decode: no matrix-core path for KV dtype %d", (int)kv_dt);
+}
+
+}  // namespace attn

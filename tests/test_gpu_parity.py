@@ -246,10 +246,17 @@ def test_decode_quantised_full(kv, T):
     check_lp(o, lse, ro, rl, f"{kv} decode T={T}")
 
 
+@pytest.fixture(params=["mfma", "valu"])
+def decode_path(request, monkeypatch):
+    """Both split kernels: matrix cores (the default for bf16 / e4m3 / int8) and vector ALUs."""
+    monkeypatch.setenv("ATTN_DECODE_PATH", request.param)
+    return request.param
+
+
 @pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "int4"])
 @pytest.mark.parametrize("paged,page_size", [(True, 16), (True, 512), (False, 0)])
 @pytest.mark.parametrize("G,D", [(1, 128), (4, 64), (5, 128), (8, 128)])
-def test_decode_ragged_edge_cases(kv, paged, page_size, G, D):
+def test_decode_ragged_edge_cases(kv, paged, page_size, G, D, decode_path):
     import oracle
     Hkv = 2
     lens = np.array([0, 1, 15, 16, 17, 513, 2000], dtype=np.int32)
@@ -257,6 +264,7 @@ def test_decode_ragged_edge_cases(kv, paged, page_size, G, D):
                              spare=3, seed=100 + G + D + page_size)
     ro, rl = oracle.decode(case)
     for ns in (0, 1, 3, 1000):
+        say(f"decode {decode_path} {kv} paged={paged} ps={page_size} G={G} D={D} splits={ns}")
         o, lse = gpu_decode(case, num_splits=ns)
         assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
         check_lp(o, lse, ro, rl, f"{kv} paged={paged} ps={page_size} G={G} D={D} splits={ns}")
@@ -278,8 +286,8 @@ def test_decode_many_sequences_mixed_lengths():
 
 @pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "int4"])
 @pytest.mark.parametrize("G,n_q,D", [(4, 2, 128), (4, 4, 128), (1, 8, 128), (2, 3, 64), (5, 2, 128), (8, 3, 128),
-                                     (1, 13, 64)])
-def test_decode_multi_token_edge_cases(kv, G, n_q, D):
+                                     (1, 13, 64), (4, 5, 128), (1, 17, 64)])
+def test_decode_multi_token_edge_cases(kv, G, n_q, D, decode_path):
     """Multi-token decode == oracle: lengths shorter than n_q (rows that see no
     key), pieces ending inside the causal tail, 16-token pages and a
     contiguous cache, over several work-unit counts."""
@@ -291,7 +299,7 @@ def test_decode_multi_token_edge_cases(kv, G, n_q, D):
                                  seed=300 + G * 10 + n_q, n_q=n_q)
         ro, rl = oracle.decode(case)
         for ns in (0, 1, 5, 1000):
-            say(f"multi-token {kv} G={G} n_q={n_q} D={D} paged={paged} units={ns}")
+            say(f"multi-token {decode_path} {kv} G={G} n_q={n_q} D={D} paged={paged} units={ns}")
             o, lse = gpu_decode(case, num_splits=ns)
             assert o.shape == ro.shape and lse.shape == rl.shape
             assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
@@ -323,7 +331,7 @@ def test_decode_multi_token_full(kv):
     check_lp(o, lse, ro, rl, f"multi-token {kv} n_q={w['n_q']} lens={lens.tolist()}")
 
 
-def test_decode_fp8_every_finite_code():
+def test_decode_fp8_every_finite_code(decode_path):
     """A cache holding every finite e4m3fn byte: the hardware decode must be OCP e4m3fn."""
     import oracle
     B, Hq, Hkv, D = 1, 1, 1, 128
@@ -337,8 +345,14 @@ def test_decode_fp8_every_finite_code():
             "page_table": None, "page_size": T, "paged": False, "scale": 1 / math.sqrt(D)}
     o, lse = gpu_decode(case)
     ro, rl = oracle.decode(case)
-    # values reach +-448*0.5: compare relative to the output scale
-    assert normwise_err(o, ro) <= 1e-3 and lse_err(lse, rl) <= 1e-3
+    # values reach +-448*0.5: compare relative to the output scale.  A wrong
+    # e4m3 decode errs by O(1); the matrix-core path rounds the softmax weights
+    # to bf16 (2^-9 relative), which over these 64 near-equal weights and
+    # values up to 224 gives ~6e-3 (the suite's normwise guard is 1e-2), the
+    # vector-ALU path keeps them in fp32
+    bound = 1e-2 if decode_path == "mfma" else 1e-3
+    say(f"fp8 every code {decode_path}: normwise={normwise_err(o, ro):.2e}")
+    assert normwise_err(o, ro) <= bound and lse_err(lse, rl) <= 1e-3
 
 
 def test_decode_equals_last_prefill_row():

@@ -42,6 +42,7 @@ PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk (dense, published 
 PEAK_FP8_TFLOPS = 5033.2  # dense fp8 matrix-core peak (published 5.0 PF)
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "exact_long_context_tiled_amd", "csrc")
+DECODE_SOURCES = ("decode.hip", "decode_mfma.hip", "decode_common.h")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -167,7 +168,8 @@ def bench_prefill_fp8(args):
     return {"workload": "llama13b_gqa_causal_fp8", "value": round(tflops, 2), "unit": "TFLOP/s",
             "ms_per_launch": round(ms, 5), "dtype": "e4m3 Q.K^T, bf16 P.V",
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
-                         "frac": round(tflops / peak, 4), "traffic": None,
+                         "frac": round(tflops / peak, 4),
+                         "traffic": recorded_traffic("prefill_fp8_llama13b_pmc_traffic.md", "prefill_fp8.hip"),
                          "peak_note": "half the flops at the fp8 peak (5.0 PF), half at the bf16 peak (2.5 PF)"}}
 
 
@@ -214,7 +216,7 @@ def bench_decode(args):
             "cache_copies": copies, "steps": steps,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": recorded_traffic("decode_paged_bf16_pmc_traffic.md", "decode.hip")}}
+                         "traffic": recorded_traffic("decode_paged_bf16_pmc_traffic.md", *DECODE_SOURCES)}}
 
 
 def bench_decode_quant(args):
@@ -278,8 +280,8 @@ def bench_decode_quant(args):
                    "cache_copies": copies, "steps": steps,
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                 "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                "traffic": recorded_traffic(f"decode_{kv}_contig_pmc_traffic.md", "decode.hip")
-                                if kv != "int4" else None}}
+                                "traffic": recorded_traffic(f"decode_{kv}_contig_pmc_traffic.md",
+                                                            *DECODE_SOURCES)}}
         del caches
     return {"workload": "quant_decode", "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "T": T, "kv": res}
 
@@ -357,7 +359,8 @@ def bench_decode_multi(args):
         res[kv] = {"value": round(gbs, 2), "unit": "GB/s", "us_per_call": round(ms * 1e3, 3), "bytes": nbytes,
                    "single_token_us_per_call": round(ms1 * 1e3, 3), "cache_copies": copies, "steps": steps,
                    "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+                                "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                "traffic": recorded_traffic(f"decode_multi_{kv}_pmc_traffic.md", *DECODE_SOURCES)}}
         del caches
     return {"workload": "multi_token_decode", "B": B, "n_q": n_q, "Hq": Hq, "Hkv": Hkv, "D": D,
             "page_size": ps, "lengths": lens.tolist(), "kv": res}

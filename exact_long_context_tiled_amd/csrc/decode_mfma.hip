@@ -475,12 +475,11 @@ template <int KV, int D>
 attn_status launch_kd(const DecodeArgs& a, hipStream_t stream) {
   auto kern = decode_mfma_kernel<KV, D>;
   const size_t lds = mfma_lds_bytes<KV, D>(a.B);
-  static bool lds_set = false;
-  if (!lds_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)mfma_lds_bytes<KV, D>(4095)) != hipSuccess)
-      return set_error(ATTN_E_DEVICE, "decode: cannot raise the LDS limit");
-    lds_set = true;
+  static size_t lds_set = 0;  // dynamic LDS limit raised so far (the length prefix grows with B)
+  if (lds > lds_set) {
+    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+      return set_error(ATTN_E_DEVICE, "decode: cannot raise the LDS limit to %zu bytes", lds);
+    lds_set = lds;
   }
   hipLaunchKernelGGL(kern, dim3(a.n_units), dim3(kThreads), lds, stream, a);
   return check_launch("decode_mfma");

@@ -29,15 +29,29 @@ attn_status check_launch(const char* what) {
 }
 
 int device_cu_count() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
+}
+
+attn_status raise_lds_limit(const void* kernel, size_t bytes, std::atomic<size_t>* raised) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(ATTN_E_DEVICE, "cannot query the current device");
+  size_t cur = raised[dev].load(std::memory_order_acquire);
+  if (bytes <= cur) return ATTN_OK;
+  if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) != hipSuccess)
+    return set_error(ATTN_E_DEVICE, "cannot raise the dynamic LDS limit to %zu bytes", bytes);
+  // keep the largest limit set (another thread may have raised it further meanwhile)
+  while (cur < bytes && !raised[dev].compare_exchange_weak(cur, bytes, std::memory_order_acq_rel)) {
+  }
+  return ATTN_OK;
 }
 
 }  // namespace attn

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <string>
 
 #include "attn.h"
@@ -24,6 +25,11 @@ attn_status check_launch(const char* what);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
+
+// Raise `kernel`'s dynamic LDS limit on the current device to at least
+// `bytes`; `raised` holds the limit already set per device (thread-safe).
+constexpr int kMaxDevices = 64;
+attn_status raise_lds_limit(const void* kernel, size_t bytes, std::atomic<size_t>* raised);
 
 // ---------------------------------------------------------------- prefill
 // One launch computes a block of n_q queries against a block of n_k keys for

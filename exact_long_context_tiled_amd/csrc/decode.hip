@@ -612,13 +612,9 @@ template <int KV, int D, int G, int TQ>
 attn_status launch_one(DecodeArgs a, hipStream_t stream) {
   const size_t lds = (size_t)(a.B + 1) * sizeof(int64_t);
   auto kern = decode_split_kernel<KV, D, G, TQ>;
-  static bool lds_set = false;  // the length prefix may take the LDS past the default dynamic limit
-  if (!lds_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)((4095 + 1) * sizeof(int64_t))) != hipSuccess)
-      return set_error(ATTN_E_DEVICE, "decode: cannot raise the LDS limit");
-    lds_set = true;
-  }
+  static std::atomic<size_t> lds_set[kMaxDevices];  // the length prefix may pass the default dynamic limit
+  attn_status st = raise_lds_limit((const void*)kern, lds, lds_set);
+  if (st != ATTN_OK) return st;
   hipLaunchKernelGGL(kern, dim3(a.n_units), dim3(kDecodeThreads), lds, stream, a);
   return check_launch("decode_split");
 }

@@ -153,6 +153,8 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
   const int n_q = a.n_q;
   const int RT = n_q * G;
   const int REC = decode_record_floats(RT, D);
+  // int8 scale arrays whose base is 16-byte aligned can be read 8 tokens at a time
+  const bool scales16 = (((uintptr_t)a.k_scale | (uintptr_t)a.v_scale) & 15) == 0;
 
   for (int64_t pos = unit * W / N; pos < x1;) {
     int lo = 0, hi = a.B - 1;
@@ -232,7 +234,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
           // inside a page): two 16-byte loads each, or clamped single loads at the end
           const int tb = g0 + 8 * j;
           const int64_t base = (tb - g0 < 16 ? base0 : base1);
-          if (tb + 8 <= tend && ((base + tb) & 3) == 0) {  // (16-byte aligned runs)
+          if (tb + 8 <= tend && scales16 && ((base + tb) & 3) == 0) {  // (16-byte aligned runs)
             const float4* kp = (const float4*)(a.k_scale + base + tb);
             const float4* vp = (const float4*)(a.v_scale + base + tb);
             kbf.ks[0] = kp[0];
@@ -475,12 +477,9 @@ template <int KV, int D>
 attn_status launch_kd(const DecodeArgs& a, hipStream_t stream) {
   auto kern = decode_mfma_kernel<KV, D>;
   const size_t lds = mfma_lds_bytes<KV, D>(a.B);
-  static size_t lds_set = 0;  // dynamic LDS limit raised so far (the length prefix grows with B)
-  if (lds > lds_set) {
-    if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
-      return set_error(ATTN_E_DEVICE, "decode: cannot raise the LDS limit to %zu bytes", lds);
-    lds_set = lds;
-  }
+  static std::atomic<size_t> lds_set[kMaxDevices];  // the length prefix grows with B
+  attn_status st = raise_lds_limit((const void*)kern, lds, lds_set);
+  if (st != ATTN_OK) return st;
   hipLaunchKernelGGL(kern, dim3(a.n_units), dim3(kThreads), lds, stream, a);
   return check_launch("decode_mfma");
 }

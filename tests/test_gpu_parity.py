@@ -306,6 +306,30 @@ def test_decode_multi_token_edge_cases(kv, G, n_q, D, decode_path):
             check_lp(o, lse, ro, rl, f"multi-token {kv} G={G} n_q={n_q} paged={paged} units={ns}")
 
 
+def test_decode_int8_scales_at_unaligned_addresses(decode_path):
+    """int8 scale arrays that start 4 bytes past a 16-byte boundary (read one by one)."""
+    import oracle
+    lens = np.array([5, 40, 700], dtype=np.int32)
+    case = gen.decode_inputs(3, 8, 2, 128, lens, kv="int8", page_size=16, seed=91)
+    ro, rl = oracle.decode(case)
+    q = to_dev(case["q"])
+    k, v = to_dev(case["k"]), to_dev(case["v"])
+    pt = to_dev(case["page_table"])
+    lens_d = to_dev(lens)
+
+    def shifted(a):
+        t = torch.empty(a.size + 1, dtype=torch.float32, device="cuda")
+        t[1:] = torch.from_numpy(a.reshape(-1)).cuda()
+        return t[1:].view(a.shape)
+
+    ks, vs = shifted(case["k_scale"]), shifted(case["v_scale"])
+    assert ks.data_ptr() % 16 == 4
+    o, lse = attn.decode_splitkv(q, k, v, lens_d, int(lens.max()), page_table=pt, k_scale=ks, v_scale=vs,
+                                 scale=case["scale"])
+    torch.cuda.synchronize()
+    check_lp(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, f"int8 unaligned scales {decode_path}")
+
+
 def test_decode_multi_one_token_is_splitkv():
     """n_q = 1 through the multi-token entry point is the single-token call, bit for bit."""
     lens = np.array([0, 7, 300, 4000], dtype=np.int32)

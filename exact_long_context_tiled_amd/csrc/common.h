@@ -105,10 +105,10 @@ __host__ __device__ inline int decode_record_floats(int rows, int D) { return ro
 size_t decode_workspace_bytes(int B, int Hkv, int rows, int D, int n_units_bound);
 // n_units == 0 picks one work-group per compute unit (at most
 // kDecodeMaxAutoUnits); the merge kernel runs after the split kernel.  The
-// split runs on the matrix cores for bf16 / e4m3 / int8 caches (unless
-// ATTN_DECODE_PATH=valu), on the vector ALUs otherwise.
+// split runs on the matrix cores for bf16 / e4m3 / int8 caches and D = 128
+// int4 caches (unless ATTN_DECODE_PATH=valu), on the vector ALUs otherwise.
 attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a, int D, int G, hipStream_t stream);
-bool decode_mfma_supported(attn_dtype kv_dt);
+bool decode_mfma_supported(attn_dtype kv_dt, int D);
 attn_status launch_decode_split_mfma(attn_dtype kv_dt, const DecodeArgs& a, int D, hipStream_t stream);
 
 // ---------------------------------------------------------------- merge

@@ -88,8 +88,10 @@ struct KvTraits<ATTN_INT4> {
 constexpr int kInt4Group = 32;  // elements per int4 scale group
 
 // The 4-bit two's-complement code at nibble e (element e of the word: bits
-// 4e .. 4e+3, low nibble of a byte first) as an int.
-__device__ __forceinline__ int int4_code(uint32_t w, int e) { return __builtin_amdgcn_sbfe((int)w, 4 * e, 4); }
+// 4e .. 4e+3, low nibble of a byte first) as an int.  (A shift pair, not the
+// bitfield-extract builtin: this compiler can convert the builtin's result to
+// float as an unsigned value.)
+__device__ __forceinline__ int int4_code(uint32_t w, int e) { return ((int)(w << (28 - 4 * e))) >> 28; }
 
 // Decode one slice into EPL floats (without scales).
 template <int KV>
@@ -678,7 +680,7 @@ attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a0, int D, int G, 
   const char* path = getenv("ATTN_DECODE_PATH");
   const bool valu = path && strcmp(path, "valu") == 0;
   attn_status st;
-  if (decode_mfma_supported(kv_dt) && !valu) {
+  if (decode_mfma_supported(kv_dt, D) && !valu) {
     st = launch_decode_split_mfma(kv_dt, a, D, stream);
   } else {
     switch (kv_dt) {

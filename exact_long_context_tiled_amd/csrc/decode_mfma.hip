@@ -1,4 +1,5 @@
-// Split-KV decode on the matrix cores (bf16, e4m3 and int8 caches).
+// Split-KV decode on the matrix cores (bf16, e4m3, int8 and, for D = 128,
+// int4 caches).
 //
 // The work split, the partial records and the log-sum-exp merge are those of
 // the vector-ALU kernel in decode.hip (flash decoding: ONNX Runtime PR #28695
@@ -24,7 +25,11 @@
 //                 (8 tokens) for e4m3 / int8, converted exactly to bf16.
 //
 // e4m3 and int8 codes become exact bf16 numbers; P is rounded to bf16 as in
-// the prefill kernels.  int8 scales (per token) multiply the fp32 scores and
+// the prefill kernels.  int4 (32-element scale groups) is dequantised with its
+// scale into bf16 (rounded): a lane quarter of the K operand is exactly one
+// group of its token, and an 8-bit transposing V read gives a lane both
+// nibbles (two dims) of one byte column for 8 tokens, i.e. two A operands
+// (even and odd dims) whose 8 tokens carry that group's per-token scales.  int8 scales (per token) multiply the fp32 scores and
 // the softmax weights; e4m3 scales (per KV head) join scale*log2(e) and the
 // output factor.  Each of the 4 waves of a work-group scans every 4th
 // 32-token block of a piece with its own online softmax; the waves are then
@@ -66,9 +71,10 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// bytes of a D-element row
 template <int KV>
-constexpr int elem_bytes() {
-  return KV == ATTN_BF16 ? 2 : 1;
+constexpr int row_bytes(int D) {
+  return KV == ATTN_BF16 ? 2 * D : KV == ATTN_INT4 ? D / 2 : D;
 }
 
 // Eight 8-bit codes (two words, element order) -> eight exact bf16 values.
@@ -96,15 +102,20 @@ __device__ __forceinline__ bf16x8 codes8_to_bf16(uint32_t w0, uint32_t w1) {
   }
 }
 
+// The 4-bit two's-complement code at bits s .. s+3 of w.  (Written as a
+// shift pair: the bitfield-extract builtin's result was converted to float as
+// unsigned by this compiler, turning negative codes into ~4e9.)
+__device__ __forceinline__ int nibble_at(uint32_t w, int s) { return ((int)(w << (28 - s))) >> 28; }
+
 template <int KV, int D>
 struct MTile {
-  static constexpr int EB = elem_bytes<KV>();
-  static constexpr int ROWB = D * EB;                 // bytes per token row
+  static constexpr int ROWB = row_bytes<KV>(D);       // bytes per token row
   static constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
   static constexpr int BYTES = kBlk * ROWB;           // one wave's V tile
   static constexpr int COPIES = BYTES / 1024;         // wave-wide 1 KiB copies per tile
   static constexpr int QD = D / 4;                    // dims per lane quarter (QK operands)
-  static constexpr int KL = QD * EB / 16;             // 16-byte K loads per token per lane
+  static constexpr int QB = row_bytes<KV>(QD);        // K bytes per token per lane quarter
+  static constexpr int KL = QB / 16;                  // 16-byte K loads per token per lane
   static constexpr int NKS = D / 32;                  // k-steps of the QK product
   static constexpr int NDB = D / 16;                  // 16-dim blocks of the PV product
   // V tiles of all waves, later overlaid by the wave partials of the combine
@@ -125,7 +136,7 @@ __device__ __forceinline__ int swz_v(int r) {
 template <int KV, int D>
 __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
   using TL = MTile<KV, D>;
-  constexpr int EB = TL::EB;
+  static_assert(KV != ATTN_INT4 || D == 128, "int4: one 32-element scale group per lane quarter");
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   char* vtiles = smem;                                     // [waves][2][BYTES]
   int64_t* pre = (int64_t*)(smem + TL::REGION);            // [B + 1]
@@ -215,6 +226,8 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
       struct Kbuf {
         uint4 k[2][TL::KL];
         float4 ks[2], vs[2];  // int8: scales of tokens 8j .. 8j+7 of the block
+        float ks4[2];         // int4: the K scale of this lane's group (group j) of its two tokens
+        float4 vs4[8];        // int4: V scales of tokens 8j + e, all 4 groups
       };
       // loads of block starting at token g0: K operands to registers, V tile to LDS
       auto issue = [&](int g0, Kbuf& kbf, char* vt) {
@@ -225,9 +238,26 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
         for (int sb = 0; sb < 2; ++sb) {
           const int tk = min(g0 + 8 * (i >> 2) + 4 * sb + (i & 3), tl);
           const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
-          const uint4* src = (const uint4*)(kb + row * TL::ROWB + TL::QD * EB * j);
+          const uint4* src = (const uint4*)(kb + row * TL::ROWB + TL::QB * j);
 #pragma unroll
           for (int u = 0; u < TL::KL; ++u) kbf.k[sb][u] = src[u];
+        }
+        if constexpr (KV == ATTN_INT4) {
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+            const int tk = min(g0 + 8 * (i >> 2) + 4 * sb + (i & 3), tl);
+            const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
+            kbf.ks4[sb] = a.k_scale[row * (D / 32) + j];
+          }
+          // V scales [row][4 groups] of tokens 8j .. 8j+7: 8 aligned 16-byte loads
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int tk = min(g0 + 8 * j + e, tl);
+            const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
+            kbf.vs4[e] = scales16 ? *(const float4*)(a.v_scale + row * 4)
+                                  : float4{a.v_scale[row * 4], a.v_scale[row * 4 + 1], a.v_scale[row * 4 + 2],
+                                           a.v_scale[row * 4 + 3]};
+          }
         }
         if constexpr (KV == ATTN_INT8) {
           // the per-token scales of this lane quarter's 8 tokens (one 8-token run
@@ -269,10 +299,18 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
       // V^T operands of a block: lane (j, i) holds dim 16*db + i of tokens 8j .. 8j+7
       struct Vops {
         bf16x8 v[TL::NDB];
+        i32x2 raw4[TL::CPR];  // int4: 8 tokens x byte i of each 16-byte chunk (= 32-dim group)
       };
       auto vread = [&](const char* vt, Vops& vo) {
         bf16x8* vop = vo.v;
-        if constexpr (KV == ATTN_BF16) {
+        if constexpr (KV == ATTN_INT4) {
+#pragma unroll
+          for (int c = 0; c < TL::CPR; ++c) {
+            const int rrow = 8 * j + (i >> 1);
+            const char* p = vt + rrow * TL::ROWB + 16 * (c ^ swz_v<KV, D>(rrow)) + 8 * (i & 1);
+            vo.raw4[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
+          }
+        } else if constexpr (KV == ATTN_BF16) {
 #pragma unroll
           for (int db = 0; db < TL::NDB; ++db) {
             const int col = 32 * db + 8 * (i & 3);  // byte within the row
@@ -306,6 +344,13 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
             bf16x8 kop;
             if constexpr (KV == ATTN_BF16) {
               kop = __builtin_bit_cast(bf16x8, kbf.k[sb][ks]);
+            } else if constexpr (KV == ATTN_INT4) {
+              // 8 nibbles of dims 8ks .. 8ks+7 of this lane's group, times the group scale
+              const uint4 wv = kbf.k[sb][0];
+              const uint32_t wd = ks == 0 ? wv.x : ks == 1 ? wv.y : ks == 2 ? wv.z : wv.w;
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                kop[e] = (__bf16)((float)nibble_at(wd, 4 * e) * kbf.ks4[sb]);
             } else {
               const uint4 wv = kbf.k[sb][ks >> 1];
               kop = (ks & 1) ? codes8_to_bf16<KV>(wv.z, wv.w) : codes8_to_bf16<KV>(wv.x, wv.y);
@@ -360,8 +405,25 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
         }
         l += ls;
         // O^T += V^T P^T
+        if constexpr (KV == ATTN_INT4) {
+          // group c: even dims 32c + 2i (low nibbles) into acc[2c], odd dims into acc[2c+1]
 #pragma unroll
-        for (int db = 0; db < TL::NDB; ++db) acc[db] = mfma16(vop[db], pf, acc[db]);
+          for (int c = 0; c < TL::CPR; ++c) {
+            bf16x8 lo8, hi8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t wd = (uint32_t)vo.raw4[c][e >> 2];
+              const float sc4 = kbf.vs4[e][c];
+              lo8[e] = (__bf16)((float)nibble_at(wd, 8 * (e & 3)) * sc4);
+              hi8[e] = (__bf16)((float)nibble_at(wd, 8 * (e & 3) + 4) * sc4);
+            }
+            acc[2 * c] = mfma16(lo8, pf, acc[2 * c]);
+            acc[2 * c + 1] = mfma16(hi8, pf, acc[2 * c + 1]);
+          }
+        } else {
+#pragma unroll
+          for (int db = 0; db < TL::NDB; ++db) acc[db] = mfma16(vop[db], pf, acc[db]);
+        }
       };
 
       // two-stage pipeline over this wave's blocks (every 4th 32-token block
@@ -412,7 +474,12 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int db = 0; db < TL::NDB; ++db)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) red_acc[(w * kRows + i) * D + 16 * db + 4 * j + q] = acc[db][q];
+        for (int q = 0; q < 4; ++q) {
+          // output dim of accumulator row 4j + q: 16*db + 4j + q, or for int4 the
+          // interleaved dims 32*(db/2) + 2*(4j + q) + db%2
+          const int d = KV == ATTN_INT4 ? 32 * (db >> 1) + 2 * (4 * j + q) + (db & 1) : 16 * db + 4 * j + q;
+          red_acc[(w * kRows + i) * D + d] = acc[db][q];
+        }
       if (j == 0) {
         red_m[w * kRows + i] = m;
         red_l[w * kRows + i] = l;
@@ -486,8 +553,8 @@ attn_status launch_kd(const DecodeArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-bool decode_mfma_supported(attn_dtype kv_dt) {
-  return kv_dt == ATTN_BF16 || kv_dt == ATTN_FP8_E4M3 || kv_dt == ATTN_INT8;
+bool decode_mfma_supported(attn_dtype kv_dt, int D) {
+  return kv_dt == ATTN_BF16 || kv_dt == ATTN_FP8_E4M3 || kv_dt == ATTN_INT8 || (kv_dt == ATTN_INT4 && D == 128);
 }
 
 attn_status launch_decode_split_mfma(attn_dtype kv_dt, const DecodeArgs& a, int D, hipStream_t stream) {
@@ -496,6 +563,9 @@ attn_status launch_decode_split_mfma(attn_dtype kv_dt, const DecodeArgs& a, int 
     case ATTN_FP8_E4M3:
       return D == 128 ? launch_kd<ATTN_FP8_E4M3, 128>(a, stream) : launch_kd<ATTN_FP8_E4M3, 64>(a, stream);
     case ATTN_INT8: return D == 128 ? launch_kd<ATTN_INT8, 128>(a, stream) : launch_kd<ATTN_INT8, 64>(a, stream);
+    case ATTN_INT4:
+      if (D == 128) return launch_kd<ATTN_INT4, 128>(a, stream);
+      break;
     default: break;
   }
   return set_error(ATTN_E_UNSUPPORTED, "decode: no matrix-core path for KV dtype %d", (int)kv_dt);

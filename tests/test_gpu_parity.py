@@ -255,7 +255,7 @@ def decode_path(request, monkeypatch):
 
 @pytest.mark.parametrize("kv", ["bf16", "int8", "fp8", "int4"])
 @pytest.mark.parametrize("paged,page_size", [(True, 16), (True, 512), (False, 0)])
-@pytest.mark.parametrize("G,D", [(1, 128), (4, 64), (5, 128), (8, 128)])
+@pytest.mark.parametrize("G,D", [(1, 128), (4, 64), (5, 128), (8, 128), (3, 128), (7, 64)])
 def test_decode_ragged_edge_cases(kv, paged, page_size, G, D, decode_path):
     import oracle
     Hkv = 2

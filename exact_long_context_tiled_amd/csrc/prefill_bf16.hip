@@ -41,12 +41,14 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Asynchronous 16-byte copy from global memory to LDS (lane i writes LDS
-// offset 16*i from the wave-uniform destination).  The builtin only exists in
-// the device compilation pass; the host pass only needs the declaration.
-__device__ __forceinline__ void copy16_to_lds(const void* src, lds_void* dst) {
+// Asynchronous 16-byte copy from a buffer to LDS: lane i reads 16 bytes at
+// byte offset voff + soff of the buffer and writes them at LDS offset 16*i
+// from the wave-uniform destination.  The builtin only exists in the device
+// compilation pass; the host pass only needs the declaration.
+constexpr int kBufDword3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff, int soff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 #endif
 }
 
@@ -172,19 +174,46 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(PrefillArgs a
   // ---- direct global -> LDS copies of one K/V tile
   const uint16_t* kbase = (const uint16_t*)a.k + b * a.k_sb + (int64_t)hk * D;
   const uint16_t* vbase = (const uint16_t*)a.v + b * a.k_sb + (int64_t)hk * D;
-  const int nk1 = (int)(a.n_k - 1);  // the host keeps n_k < 2^31 per launch
   const int cp_row = lane / TL::CPR;  // row within a copy
   const int cp_chunk = lane % TL::CPR;
+  // Copies go through buffer resources whose base moves with the tile (scalar
+  // registers), so the per-lane byte offsets below are loop-invariant.  V's
+  // swizzle does not depend on the copy index, so its copies differ only by a
+  // scalar offset.  Rows past the block are clamped onto the last key (finite
+  // data, masked below) on the one tile that reaches past it.
+  const int ksb = (int)a.k_ss * 2;  // bytes between key rows (< 2^26)
+  uint32_t koff[TL::COPIES];
+#pragma unroll
+  for (int c = 0; c < TL::COPIES; ++c) {
+    const int rr = (w * TL::COPIES + c) * TL::ROWS_PER_COPY + cp_row;
+    koff[c] = (uint32_t)(rr * ksb + 16 * (cp_chunk ^ swz_k<D>(rr)));
+  }
+  const int rv0 = w * TL::COPIES * TL::ROWS_PER_COPY + cp_row;
+  const uint32_t voff = (uint32_t)(rv0 * ksb + 16 * (cp_chunk ^ swz_v<D>(rv0)));
   auto issue_tile = [&](int t, char* kst) {
     char* vst = kst + TL::BYTES;
+    const int64_t k0 = (int64_t)t * kBK;
+    const uint64_t rem = (uint64_t)(a.n_k - k0) * (uint64_t)ksb;
+    const int nrec = (int)(uint32_t)min(rem, (uint64_t)0xFFFFFFFFu);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + k0 * a.k_ss), (short)0, nrec, kBufDword3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + k0 * a.k_ss), (short)0, nrec, kBufDword3);
+    if (k0 + kBK <= a.n_k) {
 #pragma unroll
-    for (int c = 0; c < TL::COPIES; ++c) {
-      const int q = w * TL::COPIES + c;  // copy index within the tile
-      const int rr = q * TL::ROWS_PER_COPY + cp_row;
-      const int j = min(t * kBK + rr, nk1);  // keys past the block: finite copies, masked below
-      const int64_t row_off = (int64_t)j * a.k_ss;
-      copy16_to_lds(kbase + row_off + 8 * (cp_chunk ^ swz_k<D>(rr)), (lds_void*)(kst + q * 1024));
-      copy16_to_lds(vbase + row_off + 8 * (cp_chunk ^ swz_v<D>(rr)), (lds_void*)(vst + q * 1024));
+      for (int c = 0; c < TL::COPIES; ++c) {
+        const int q = w * TL::COPIES + c;  // copy index within the tile
+        copy16_to_lds(rk, (lds_void*)(kst + q * 1024), koff[c], 0);
+        copy16_to_lds(rv, (lds_void*)(vst + q * 1024), voff, c * TL::ROWS_PER_COPY * ksb);
+      }
+    } else {
+      const int last = (int)(a.n_k - 1 - k0);
+#pragma unroll
+      for (int c = 0; c < TL::COPIES; ++c) {
+        const int q = w * TL::COPIES + c;
+        const int rr = q * TL::ROWS_PER_COPY + cp_row;
+        const int j = min(rr, last);
+        copy16_to_lds(rk, (lds_void*)(kst + q * 1024), (uint32_t)(j * ksb + 16 * (cp_chunk ^ swz_k<D>(rr))), 0);
+        copy16_to_lds(rv, (lds_void*)(vst + q * 1024), (uint32_t)(j * ksb + 16 * (cp_chunk ^ swz_v<D>(rr))), 0);
+      }
     }
   };
 

@@ -44,9 +44,13 @@ typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 
-__device__ __forceinline__ void copy16_to_lds(const void* src, lds_void* dst) {
+// Asynchronous 16-byte copy from a buffer to LDS: lane i reads 16 bytes at
+// byte offset voff of the buffer and writes them at LDS offset 16*i from the
+// wave-uniform destination (the builtin exists in the device pass only).
+constexpr int kBufDword3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, lds_void* dst, uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, 0, 0, 0);
 #endif
 }
 
@@ -163,19 +167,33 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fp8_kernel(PrefillArgs a,
 
   const uint8_t* kbase = (const uint8_t*)a.k + b * a.k_sb + (int64_t)hk * D;
   const uint8_t* vbase = (const uint8_t*)a.v + b * a.k_sb + (int64_t)hk * D;
-  const int nk1 = (int)(a.n_k - 1);
   const int cp_row = lane / TL::CPR;
   const int cp_chunk = lane % TL::CPR;
+  // Copies go through buffer resources whose base moves with the tile (scalar
+  // registers); the per-lane byte offsets are loop-invariant.  The rows of
+  // one lane's copies differ by multiples of the chunks per row, so K and V
+  // share one swizzled chunk offset.  Rows past the block are clamped onto
+  // the last key (finite data, masked below): row offsets grow with the row,
+  // so the clamp is a min on the offset.
+  const int ksb = (int)a.k_ss;  // bytes between key rows (< 2^24)
+  int rowb[TL::COPIES];
+#pragma unroll
+  for (int c = 0; c < TL::COPIES; ++c) rowb[c] = ((w * TL::COPIES + c) * TL::ROWS_PER_COPY + cp_row) * ksb;
+  const int chb = 16 * (cp_chunk ^ swz<D>(w * TL::COPIES * TL::ROWS_PER_COPY + cp_row));
   auto issue_tile = [&](int t, char* kst) {
     char* vst = kst + TL::BYTES;
+    const int64_t k0 = (int64_t)t * kBK;
+    const uint64_t remb = (uint64_t)(a.n_k - k0) * (uint64_t)ksb;
+    const int nrec = (int)(uint32_t)min(remb, (uint64_t)0xFFFFFFFFu);
+    const int lastb = (int)min((int64_t)(kBK - 1), a.n_k - 1 - k0) * ksb;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + k0 * a.k_ss), (short)0, nrec, kBufDword3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + k0 * a.k_ss), (short)0, nrec, kBufDword3);
 #pragma unroll
     for (int c = 0; c < TL::COPIES; ++c) {
       const int q = w * TL::COPIES + c;
-      const int rr = q * TL::ROWS_PER_COPY + cp_row;
-      const int j = min(t * kBK + rr, nk1);  // keys past the block: finite copies, masked below
-      const int64_t row_off = (int64_t)j * a.k_ss;
-      copy16_to_lds(kbase + row_off + 16 * (cp_chunk ^ swz<D>(rr)), (lds_void*)(kst + q * 1024));
-      copy16_to_lds(vbase + row_off + 16 * (cp_chunk ^ swz<D>(rr)), (lds_void*)(vst + q * 1024));
+      const uint32_t off = (uint32_t)(min(rowb[c], lastb) + chb);
+      copy16_to_lds(rk, (lds_void*)(kst + q * 1024), off);
+      copy16_to_lds(rv, (lds_void*)(vst + q * 1024), off);
     }
   };
 

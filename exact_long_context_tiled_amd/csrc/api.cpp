@@ -188,8 +188,9 @@ attn_status decode_impl(attn_dtype kv_dt, const void* q, const void* k_cache, co
     if (page_size < max_kv_len)
       return set_error(ATTN_E_INVALID, "decode: contiguous cache needs page_size >= max_kv_len");
   }
-  // group positions times unit counts must stay inside int64
-  const double groups = (double)B * Hkv * ((max_kv_len + kDecodeGroup - 1) / kDecodeGroup);
+  // split positions (groups plus the per-segment charge) times unit counts
+  // must stay inside int64
+  const double groups = (double)B * Hkv * ((max_kv_len + kDecodeGroup - 1) / kDecodeGroup + kDecodeMaxPieceGroups);
   if (groups * (num_splits > 0 ? num_splits : kDecodeMaxAutoUnits) > 4e18)
     return set_error(ATTN_E_UNSUPPORTED, "decode: batch too large");
   const size_t need = decode_ws(B, Hq, Hkv, D, n_q, max_kv_len, num_splits);

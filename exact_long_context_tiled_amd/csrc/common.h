@@ -88,6 +88,7 @@ struct DecodeArgs {
   int G;        // Hq / Hkv
   int n_q;      // query tokens per sequence (rows of the segment: n_q * G)
   int n_units;  // N
+  int piece_groups;  // groups each non-empty segment is charged in the split (matrix-core kernel; else 0)
   float scale_log2;
   float* part;       // records [N + B*Hkv - 1][R*D + pad16(R)], R = n_q*G: O rows, then lse (log2)
   int32_t* seg_info; // [B*Hkv][2]: first record, record count (written by the segment's first unit)
@@ -98,11 +99,21 @@ struct DecodeArgs {
 constexpr int kDecodeGroup = 16;          // tokens per group (>= tokens per wave load step)
 constexpr int kDecodeMaxAutoUnits = 2048; // upper bound of the automatic unit count
 constexpr int kDecodeMaxUnits = 65535;
+constexpr int kDecodeMaxPieceGroups = 4096;  // bound of DecodeArgs::piece_groups
 
 // Floats of one partial record of `rows` query rows: O rows, then the rows' lse
 // padded to a multiple of 16.
 __host__ __device__ inline int decode_record_floats(int rows, int D) { return rows * D + (rows + 15) / 16 * 16; }
 size_t decode_workspace_bytes(int B, int Hkv, int rows, int D, int n_units_bound);
+// K + V cache bytes of one token of one KV head, scales included.
+inline int64_t decode_token_bytes(attn_dtype kv_dt, int D) {
+  switch (kv_dt) {
+    case ATTN_BF16: return 4 * (int64_t)D;
+    case ATTN_INT8: return 2 * (int64_t)D + 8;                      // + per-token fp32 scales
+    case ATTN_INT4: return (int64_t)D + 2 * (int64_t)(D / 32) * 4;  // nibbles + group scales
+    default: return 2 * (int64_t)D;                                 // e4m3 (per-head scales)
+  }
+}
 // n_units == 0 picks one work-group per compute unit (at most
 // kDecodeMaxAutoUnits); the merge kernel runs after the split kernel.  The
 // split runs on the matrix cores for bf16 / e4m3 / int8 caches and D = 128

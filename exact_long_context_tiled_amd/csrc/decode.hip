@@ -245,7 +245,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
   constexpr int64_t RB = Tr::row_bytes(D);  // bytes of one token's K (or V) row
   constexpr int kStride = kDecodeWaves * TPI;  // tokens between a wave's consecutive iterations
 
-  group_prefix<kDecodeThreads>(a.kv_lens, a.B, a.max_kv_len, pre, wsum);
+  group_prefix<kDecodeThreads>(a.kv_lens, a.B, a.max_kv_len, 0, pre, wsum);
   const int64_t W = pre[a.B] * a.Hkv;
   // never more units than groups, so that every unit owns at least one group
   // and the records of a segment are the consecutive units that cover it
@@ -680,7 +680,20 @@ attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a0, int D, int G, 
   const char* path = getenv("ATTN_DECODE_PATH");
   const bool valu = path && strcmp(path, "valu") == 0;
   attn_status st;
+  a.piece_groups = 0;
   if (decode_mfma_supported(kv_dt, D) && !valu) {
+    // Each piece of a run (a segment, or the part of one inside the run) has
+    // a fixed cost on the matrix-core kernel: its pipeline start, the wave
+    // combine and the record, ~6 us measured, about what one work-group
+    // streams in that time (~144 KB).  Charging every segment that many
+    // groups in the split gives a run that reaches into another segment
+    // correspondingly fewer keys, so work-groups with several pieces finish
+    // with the others.
+    const int64_t tok = decode_token_bytes(kv_dt, D) * kDecodeGroup;  // K + V bytes of one group, one KV head
+    int64_t cost = 144 << 10;
+    const char* env = getenv("ATTN_DECODE_PIECE_BYTES");
+    if (env && atoll(env) >= 0) cost = atoll(env);
+    a.piece_groups = (int)std::min<int64_t>(kDecodeMaxPieceGroups, (cost + tok - 1) / tok);
     st = launch_decode_split_mfma(kv_dt, a, D, stream);
   } else {
     switch (kv_dt) {

@@ -29,17 +29,24 @@ __device__ __forceinline__ void lane_pair(float x, float& a, float& b) {
 
 __device__ __forceinline__ int clamp_len(int t, int max_len) { return min(max(t, 0), max_len); }
 
-// pre[b] = groups of all segments of sequences < b (per KV head), pre[B] = total;
-// computed by the whole work-group into LDS.
+// Groups one segment of a sequence of length t occupies in the split: its
+// 16-token groups plus `charge` more when it is not empty.
+__device__ __forceinline__ int64_t seg_slots(int t, int charge) {
+  const int g = (t + kDecodeGroup - 1) / kDecodeGroup;
+  return g > 0 ? (int64_t)g + charge : 0;
+}
+
+// pre[b] = slots of all segments of sequences < b (per KV head), pre[B] =
+// total; computed by the whole work-group into LDS.
 template <int THREADS>
-__device__ void group_prefix(const int32_t* __restrict__ lens, int B, int max_len, int64_t* pre,
+__device__ void group_prefix(const int32_t* __restrict__ lens, int B, int max_len, int charge, int64_t* pre,
                              int64_t* wsum) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int per = (B + THREADS - 1) / THREADS;
   const int b0 = tid * per;
   int64_t s = 0;
   for (int k = 0; k < per; ++k)
-    if (b0 + k < B) s += (clamp_len(lens[b0 + k], max_len) + kDecodeGroup - 1) / kDecodeGroup;
+    if (b0 + k < B) s += seg_slots(clamp_len(lens[b0 + k], max_len), charge);
   int64_t x = s;  // inclusive scan over the wave
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -54,7 +61,7 @@ __device__ void group_prefix(const int32_t* __restrict__ lens, int B, int max_le
   for (int k = 0; k < per; ++k) {
     if (b0 + k < B) {
       pre[b0 + k] = run;
-      run += (clamp_len(lens[b0 + k], max_len) + kDecodeGroup - 1) / kDecodeGroup;
+      run += seg_slots(clamp_len(lens[b0 + k], max_len), charge);
     }
   }
   if (tid == THREADS - 1) pre[B] = base + x;

@@ -154,12 +154,20 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
   char* vt0 = vtiles + (2 * w) * TL::BYTES;
   char* vt1 = vt0 + TL::BYTES;
 
-  group_prefix<kThreads>(a.kv_lens, a.B, a.max_kv_len, pre, wsum);
+  // The split: segment (b, hk) occupies piece_groups charged slots followed
+  // by its 16-token groups; all segments laid end to end (W slots) are cut
+  // into N equal runs [floor(u W / N), floor((u + 1) W / N)).
+  group_prefix<kThreads>(a.kv_lens, a.B, a.max_kv_len, a.piece_groups, pre, wsum);
   const int64_t W = pre[a.B] * a.Hkv;
   const int64_t N = a.n_units < W ? (int64_t)a.n_units : W;
   const int unit = blockIdx.x;
   if (unit >= N) return;
-  const int64_t x1 = (unit + 1) * W / N;
+  // W = qd N + rw, so floor(u W / N) = u qd + floor(u rw / N), the last term
+  // in 32 bits (u, rw < N <= 65535)
+  const int64_t qd = W / N;
+  const uint32_t rw = (uint32_t)(W - qd * N);
+  const int64_t x0 = (int64_t)unit * qd + (int64_t)((uint32_t)unit * rw / (uint32_t)N);
+  const int64_t x1 = (int64_t)(unit + 1) * qd + (int64_t)((uint32_t)(unit + 1) * rw / (uint32_t)N);
   const int G = a.G;
   const int n_q = a.n_q;
   const int RT = n_q * G;
@@ -167,7 +175,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
   // int8 scale arrays whose base is 16-byte aligned can be read 8 tokens at a time
   const bool scales16 = (((uintptr_t)a.k_scale | (uintptr_t)a.v_scale) & 15) == 0;
 
-  for (int64_t pos = unit * W / N; pos < x1;) {
+  for (int64_t pos = x0; pos < x1;) {
     int lo = 0, hi = a.B - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -176,14 +184,23 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
     }
     const int b = __builtin_amdgcn_readfirstlane(lo);
     const int64_t sbase = pre[b] * a.Hkv;
-    const int ng = (int)(pre[b + 1] - pre[b]);
-    const int hk = __builtin_amdgcn_readfirstlane((int)((pos - sbase) / ng));
-    const int j0 = (int)(pos - sbase - (int64_t)hk * ng);
-    const int64_t seg_end = sbase + (int64_t)(hk + 1) * ng;
+    const int ns = (int)(pre[b + 1] - pre[b]);  // slots of one segment of b (> 0: b holds pos)
+    const int64_t off = pos - sbase;
+    const int hk = __builtin_amdgcn_readfirstlane(off <= 0x7fffffff ? (int)((uint32_t)off / (uint32_t)ns)
+                                                                      : (int)(off / ns));
+    const int64_t sstart = sbase + (int64_t)hk * ns;
+    const int64_t seg_end = sstart + ns;
     const int64_t pend = seg_end < x1 ? seg_end : x1;
+    const int64_t gstart = sstart + a.piece_groups;  // the segment's first group
+    if (pend <= gstart) {  // the run holds only charged slots of this segment
+      pos = pend;
+      continue;
+    }
+    const int64_t pg = pos > gstart ? pos : gstart;
+    const int j0 = (int)(pg - gstart);
     const int T = clamp_len(a.kv_lens[b], a.max_kv_len);
     const int t0 = __builtin_amdgcn_readfirstlane(j0 * kDecodeGroup);
-    const int t1 = __builtin_amdgcn_readfirstlane(min(T, (j0 + (int)(pend - pos)) * kDecodeGroup));
+    const int t1 = __builtin_amdgcn_readfirstlane(min(T, (j0 + (int)(pend - pg)) * kDecodeGroup));
     const int seg = b * a.Hkv + hk;
     const bool whole = j0 == 0 && pend == seg_end;
     float smul = a.scale_log2;

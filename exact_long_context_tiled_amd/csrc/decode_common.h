@@ -37,10 +37,11 @@ __device__ __forceinline__ int64_t seg_slots(int t, int charge) {
 }
 
 // pre[b] = slots of all segments of sequences < b (per KV head), pre[B] =
-// total; computed by the whole work-group into LDS.
+// total; computed by the whole work-group into LDS, with the clamped lengths
+// in len_out[b] when it is not null.
 template <int THREADS>
 __device__ void group_prefix(const int32_t* __restrict__ lens, int B, int max_len, int charge, int64_t* pre,
-                             int64_t* wsum) {
+                             int64_t* wsum, int* len_out = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int per = (B + THREADS - 1) / THREADS;
   const int b0 = tid * per;
@@ -60,8 +61,10 @@ __device__ void group_prefix(const int32_t* __restrict__ lens, int B, int max_le
   int64_t run = base + x - s;
   for (int k = 0; k < per; ++k) {
     if (b0 + k < B) {
+      const int t = clamp_len(lens[b0 + k], max_len);
       pre[b0 + k] = run;
-      run += seg_slots(clamp_len(lens[b0 + k], max_len), charge);
+      if (len_out) len_out[b0 + k] = t;
+      run += seg_slots(t, charge);
     }
   }
   if (tid == THREADS - 1) pre[B] = base + x;

@@ -102,10 +102,52 @@ __device__ __forceinline__ bf16x8 codes8_to_bf16(uint32_t w0, uint32_t w1) {
   }
 }
 
-// The 4-bit two's-complement code at bits s .. s+3 of w.  (Written as a
-// shift pair: the bitfield-extract builtin's result was converted to float as
-// unsigned by this compiler, turning negative codes into ~4e9.)
-__device__ __forceinline__ int nibble_at(uint32_t w, int s) { return ((int)(w << (28 - s))) >> 28; }
+// int4 codes as exact bf16 integers without arithmetic per element: for a
+// 4-bit two's-complement code n, v = code ^ 8 = n + 8 lies in [0, 15], and the
+// bf16 bit pattern 0x4300 | v is the value 128 + v = n + 136 (exponent 2^7,
+// v in the low mantissa bits).  The offset 136 is taken off afterwards by a
+// product with the constant operand kNeg136 below.
+constexpr uint32_t kNibMask2 = 0x000F000Fu;
+constexpr uint32_t kMagic2 = 0x43004300u;
+constexpr uint32_t kFlip8 = 0x88888888u;
+constexpr uint16_t kBf16Neg136 = 0xC308u;
+
+__device__ __forceinline__ uint32_t nib_pair(uint32_t x, int sh) { return ((x >> sh) & kNibMask2) | kMagic2; }
+
+// The 8 codes of w (code e at bits 4e .. 4e+3), as n + 136, in the element
+// order 0, 4, 1, 5, 2, 6, 3, 7 (nib_pair of a shift takes codes e and e + 4).
+__device__ __forceinline__ bf16x8 nib8_strided(uint32_t w) {
+  const uint32_t x = w ^ kFlip8;
+  return __builtin_bit_cast(bf16x8, uint4{nib_pair(x, 0), nib_pair(x, 4), nib_pair(x, 8), nib_pair(x, 12)});
+}
+
+// 4x4 transpose of dwords across the lane quarters: lane (j, i) holds d[c]
+// of quarter j on entry and quarter c's d[j] on exit (permlane32_swap
+// exchanges the upper half of its first operand with the lower half of its
+// second; permlane16_swap the odd 16-lane rows of the first with the even
+// rows of the second).
+__device__ __forceinline__ void quarter_transpose(uint32_t (&d)[4]) {
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(d[0], d[2], false, false);
+    d[0] = r[0];
+    d[2] = r[1];
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(d[1], d[3], false, false);
+    d[1] = r[0];
+    d[3] = r[1];
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(d[0], d[1], false, false);
+    d[0] = r[0];
+    d[1] = r[1];
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(d[2], d[3], false, false);
+    d[2] = r[0];
+    d[3] = r[1];
+  }
+}
 
 template <int KV, int D>
 struct MTile {
@@ -121,7 +163,7 @@ struct MTile {
   // V tiles of all waves, later overlaid by the wave partials of the combine
   static constexpr int TILES = kWaves * 2 * BYTES;
   static constexpr int RED = (kWaves * kRows * D + 2 * kWaves * kRows) * 4;
-  static constexpr int REGION = (TILES > RED ? TILES : RED + 255) / 256 * 256;
+  static constexpr int REGION = ((TILES > RED ? TILES : RED) + 255) / 256 * 256;
 };
 
 // V tile swizzle (16-byte chunk c of row r sits at c ^ swz(r)), chosen so the
@@ -140,6 +182,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   char* vtiles = smem;                                     // [waves][2][BYTES]
   int64_t* pre = (int64_t*)(smem + TL::REGION);            // [B + 1]
+  int* lens_s = (int*)(pre + a.B + 1);                     // [B] clamped lengths
   __shared__ int64_t wsum[kWaves];
   // wave partials for the combine, overlaid on the V tiles once a pass is done
   float* red_acc = (float*)smem;                           // [waves][kRows][D]
@@ -157,7 +200,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
   // The split: segment (b, hk) occupies piece_groups charged slots followed
   // by its 16-token groups; all segments laid end to end (W slots) are cut
   // into N equal runs [floor(u W / N), floor((u + 1) W / N)).
-  group_prefix<kThreads>(a.kv_lens, a.B, a.max_kv_len, a.piece_groups, pre, wsum);
+  group_prefix<kThreads>(a.kv_lens, a.B, a.max_kv_len, a.piece_groups, pre, wsum, lens_s);
   const int64_t W = pre[a.B] * a.Hkv;
   const int64_t N = a.n_units < W ? (int64_t)a.n_units : W;
   const int unit = blockIdx.x;
@@ -198,7 +241,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
     }
     const int64_t pg = pos > gstart ? pos : gstart;
     const int j0 = (int)(pg - gstart);
-    const int T = clamp_len(a.kv_lens[b], a.max_kv_len);
+    const int T = lens_s[b];
     const int t0 = __builtin_amdgcn_readfirstlane(j0 * kDecodeGroup);
     const int t1 = __builtin_amdgcn_readfirstlane(min(T, (j0 + (int)(pend - pg)) * kDecodeGroup));
     const int seg = b * a.Hkv + hk;
@@ -218,13 +261,27 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
       const int tend = __builtin_amdgcn_readfirstlane(
           max(t0, min(t1, T - (n_q - 1 - (r0 + n_rows - 1) / G))));  // past the last key any row reads
 
-      // Q operand: dims QD*j .. of the lane's row
+      // Q operand: dims QD*j .. of the lane's row; for int4, step ks takes
+      // dims 32ks + 8j .. 32ks + 8j + 7 (scale group ks) in the element order
+      // of nib8_strided, and qoff[ks] = -136 x (the row's sum over group ks)
       bf16x8 qf[TL::NKS];
+      f32x4 qoff[KV == ATTN_INT4 ? TL::NKS : 1];
       {
-        const bf16x8* qp = (const bf16x8*)((const uint16_t*)a.q +
-                                           (((int64_t)b * n_q + sq) * a.Hq + (int64_t)hk * G + g) * D + TL::QD * j);
+        const uint16_t* qrow = (const uint16_t*)a.q + (((int64_t)b * n_q + sq) * a.Hq + (int64_t)hk * G + g) * D;
+        if constexpr (KV == ATTN_INT4) {
+          const uint16_t c = kBf16Neg136;
+          const bf16x8 neg136 = __builtin_bit_cast(bf16x8, uint4{c * 0x10001u, c * 0x10001u, c * 0x10001u, c * 0x10001u});
 #pragma unroll
-        for (int ks = 0; ks < TL::NKS; ++ks) qf[ks] = qp[ks];
+          for (int ks = 0; ks < TL::NKS; ++ks) {
+            const bf16x8 raw = *(const bf16x8*)(qrow + 32 * ks + 8 * j);
+            qf[ks] = __builtin_shufflevector(raw, raw, 0, 4, 1, 5, 2, 6, 3, 7);
+            qoff[ks] = mfma16(neg136, qf[ks], f32x4{0.f, 0.f, 0.f, 0.f});
+          }
+        } else {
+          const bf16x8* qp = (const bf16x8*)(qrow + TL::QD * j);
+#pragma unroll
+          for (int ks = 0; ks < TL::NKS; ++ks) qf[ks] = qp[ks];
+        }
       }
       f32x4 acc[TL::NDB];
 #pragma unroll
@@ -243,7 +300,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
       struct Kbuf {
         uint4 k[2][TL::KL];
         float4 ks[2], vs[2];  // int8: scales of tokens 8j .. 8j+7 of the block
-        float ks4[2];         // int4: the K scale of this lane's group (group j) of its two tokens
+        float4 ks4[8];        // int4: K scales of tokens 8j + e, all 4 groups
         float4 vs4[8];        // int4: V scales of tokens 8j + e, all 4 groups
       };
       // loads of block starting at token g0: K operands to registers, V tile to LDS
@@ -260,20 +317,20 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
           for (int u = 0; u < TL::KL; ++u) kbf.k[sb][u] = src[u];
         }
         if constexpr (KV == ATTN_INT4) {
-#pragma unroll
-          for (int sb = 0; sb < 2; ++sb) {
-            const int tk = min(g0 + 8 * (i >> 2) + 4 * sb + (i & 3), tl);
-            const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
-            kbf.ks4[sb] = a.k_scale[row * (D / 32) + j];
-          }
-          // V scales [row][4 groups] of tokens 8j .. 8j+7: 8 aligned 16-byte loads
+          // K and V scales [row][4 groups] of tokens 8j .. 8j+7: aligned 16-byte loads
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const int tk = min(g0 + 8 * j + e, tl);
             const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
-            kbf.vs4[e] = scales16 ? *(const float4*)(a.v_scale + row * 4)
-                                  : float4{a.v_scale[row * 4], a.v_scale[row * 4 + 1], a.v_scale[row * 4 + 2],
-                                           a.v_scale[row * 4 + 3]};
+            if (scales16) {
+              kbf.ks4[e] = *(const float4*)(a.k_scale + row * 4);
+              kbf.vs4[e] = *(const float4*)(a.v_scale + row * 4);
+            } else {
+              const float* kp = a.k_scale + row * 4;
+              const float* vp = a.v_scale + row * 4;
+              kbf.ks4[e] = float4{kp[0], kp[1], kp[2], kp[3]};
+              kbf.vs4[e] = float4{vp[0], vp[1], vp[2], vp[3]};
+            }
           }
         }
         if constexpr (KV == ATTN_INT8) {
@@ -353,32 +410,47 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
       auto consume = [&](int g0, const Kbuf& kbf, const Vops& vo) {
         const bf16x8* vop = vo.v;
         // S^T = K Q^T for the two 16-token sub-blocks
-        f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-          for (int ks = 0; ks < TL::NKS; ++ks) {
-            bf16x8 kop;
-            if constexpr (KV == ATTN_BF16) {
-              kop = __builtin_bit_cast(bf16x8, kbf.k[sb][ks]);
-            } else if constexpr (KV == ATTN_INT4) {
-              // 8 nibbles of dims 8ks .. 8ks+7 of this lane's group, times the group scale
-              const uint4 wv = kbf.k[sb][0];
-              const uint32_t wd = ks == 0 ? wv.x : ks == 1 ? wv.y : ks == 2 ? wv.z : wv.w;
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                kop[e] = (__bf16)((float)nibble_at(wd, 4 * e) * kbf.ks4[sb]);
-            } else {
-              const uint4 wv = kbf.k[sb][ks >> 1];
-              kop = (ks & 1) ? codes8_to_bf16<KV>(wv.z, wv.w) : codes8_to_bf16<KV>(wv.x, wv.y);
-            }
-            s[sb] = mfma16(kop, qf[ks], s[sb]);
-          }
-        }
         // scores of tokens 8j + e of the block (e = 4*sb + register), this lane's row
         float sc[8];
+        if constexpr (KV == ATTN_INT4) {
+          // One product per scale group: after the transpose, dword ks of the
+          // lane's 16 bytes holds dims 32ks + 8j .. of its token (group ks),
+          // and the product starts from qoff[ks], which takes the 136 offset
+          // of the codes off.  A token's score is then the sum over groups of
+          // its group scale times the group's product.
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sc[e] = s[e >> 2][e & 3];
+          for (int sb = 0; sb < 2; ++sb) {
+            const uint4 wv = kbf.k[sb][0];
+            uint32_t d[4] = {wv.x, wv.y, wv.z, wv.w};
+            quarter_transpose(d);
+            f32x4 sg[TL::NKS];
+#pragma unroll
+            for (int ks = 0; ks < TL::NKS; ++ks) sg[ks] = mfma16(nib8_strided(d[ks]), qf[ks], qoff[ks]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float4 k4 = kbf.ks4[4 * sb + r];
+              sc[4 * sb + r] = k4.x * sg[0][r] + k4.y * sg[1][r] + k4.z * sg[2][r] + k4.w * sg[3][r];
+            }
+          }
+        } else {
+          f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+            for (int ks = 0; ks < TL::NKS; ++ks) {
+              bf16x8 kop;
+              if constexpr (KV == ATTN_BF16) {
+                kop = __builtin_bit_cast(bf16x8, kbf.k[sb][ks]);
+              } else {
+                const uint4 wv = kbf.k[sb][ks >> 1];
+                kop = (ks & 1) ? codes8_to_bf16<KV>(wv.z, wv.w) : codes8_to_bf16<KV>(wv.x, wv.y);
+              }
+              s[sb] = mfma16(kop, qf[ks], s[sb]);
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc[e] = s[e >> 2][e & 3];
+        }
         float vsc[8];
         if constexpr (KV == ATTN_INT8) {
 #pragma unroll
@@ -412,30 +484,39 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
         }
         const float m_use = m == -INFINITY ? 0.f : m;
         bf16x8 pf;
+        float pv[8];
         float ls = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float p = __builtin_amdgcn_exp2f(fmaf(sc[e], smul, -m_use));
           ls += p;
+          pv[e] = p;
           if constexpr (KV == ATTN_INT8) p = sc[e] == -INFINITY ? 0.f : p * vsc[e];
           pf[e] = (__bf16)p;
         }
         l += ls;
         // O^T += V^T P^T
         if constexpr (KV == ATTN_INT4) {
-          // group c: even dims 32c + 2i (low nibbles) into acc[2c], odd dims into acc[2c+1]
+          // Group c: even dims 32c + 2i (low nibbles) into acc[2c], odd dims
+          // into acc[2c+1].  The codes enter as n + 136 (byte pairs 0, 2 and
+          // 1, 3 of each dword: token order 0, 2, 1, 3, 4, 6, 5, 7 in both
+          // operands), each token's V scale of group c goes into its weight,
+          // and a product with the constant -136 takes the offset off.
+          const uint16_t cn = kBf16Neg136;
+          const bf16x8 neg136 = __builtin_bit_cast(bf16x8, uint4{cn * 0x10001u, cn * 0x10001u, cn * 0x10001u, cn * 0x10001u});
 #pragma unroll
           for (int c = 0; c < TL::CPR; ++c) {
-            bf16x8 lo8, hi8;
+            constexpr int tok[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+            bf16x8 pc;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t wd = (uint32_t)vo.raw4[c][e >> 2];
-              const float sc4 = kbf.vs4[e][c];
-              lo8[e] = (__bf16)((float)nibble_at(wd, 8 * (e & 3)) * sc4);
-              hi8[e] = (__bf16)((float)nibble_at(wd, 8 * (e & 3) + 4) * sc4);
-            }
-            acc[2 * c] = mfma16(lo8, pf, acc[2 * c]);
-            acc[2 * c + 1] = mfma16(hi8, pf, acc[2 * c + 1]);
+            for (int k = 0; k < 8; ++k) pc[k] = (__bf16)(pv[tok[k]] * kbf.vs4[tok[k]][c]);
+            const uint32_t x0 = (uint32_t)vo.raw4[c][0] ^ kFlip8, x1 = (uint32_t)vo.raw4[c][1] ^ kFlip8;
+            const bf16x8 lo8 = __builtin_bit_cast(bf16x8, uint4{nib_pair(x0, 0), nib_pair(x0, 8), nib_pair(x1, 0), nib_pair(x1, 8)});
+            const bf16x8 hi8 = __builtin_bit_cast(bf16x8, uint4{nib_pair(x0, 4), nib_pair(x0, 12), nib_pair(x1, 4), nib_pair(x1, 12)});
+            acc[2 * c] = mfma16(lo8, pc, acc[2 * c]);
+            acc[2 * c] = mfma16(neg136, pc, acc[2 * c]);
+            acc[2 * c + 1] = mfma16(hi8, pc, acc[2 * c + 1]);
+            acc[2 * c + 1] = mfma16(neg136, pc, acc[2 * c + 1]);
           }
         } else {
 #pragma unroll
@@ -554,7 +635,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
 
 template <int KV, int D>
 size_t mfma_lds_bytes(int B) {
-  return (size_t)MTile<KV, D>::REGION + (size_t)(B + 1) * sizeof(int64_t);
+  return (size_t)MTile<KV, D>::REGION + (size_t)(B + 1) * sizeof(int64_t) + (size_t)B * sizeof(int);
 }
 
 template <int KV, int D>

@@ -160,10 +160,14 @@ struct MTile {
   static constexpr int KL = QB / 16;                  // 16-byte K loads per token per lane
   static constexpr int NKS = D / 32;                  // k-steps of the QK product
   static constexpr int NDB = D / 16;                  // 16-dim blocks of the PV product
-  // V tiles of all waves, later overlaid by the wave partials of the combine
-  static constexpr int TILES = kWaves * 2 * BYTES;
-  static constexpr int RED = (kWaves * kRows * D + 2 * kWaves * kRows) * 4;
-  static constexpr int REGION = ((TILES > RED ? TILES : RED) + 255) / 256 * 256;
+  // V-tile stages per wave: with small tiles (8-bit and 4-bit caches) two
+  // blocks' loads are kept in flight behind the one being consumed
+  static constexpr int STAGES = BYTES <= 4096 ? 3 : 2;
+  // vector-memory operations of one block's loads (the fewest of their forms:
+  // K operands, scales, V copies)
+  static constexpr int OPS = 2 * KL + COPIES + (KV == ATTN_INT8 ? 4 : KV == ATTN_INT4 ? 16 : 0);
+  // wave partials of the combine (dynamic LDS, before the length prefix)
+  static constexpr int RED = ((kWaves * kRows * D + 2 * kWaves * kRows) * 4 + 255) / 256 * 256;
 };
 
 // V tile swizzle (16-byte chunk c of row r sits at c ^ swz(r)), chosen so the
@@ -179,12 +183,16 @@ template <int KV, int D>
 __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
   using TL = MTile<KV, D>;
   static_assert(KV != ATTN_INT4 || D == 128, "int4: one 32-element scale group per lane quarter");
+  // V-tile stages, one array each (so the compiler tells copies into one
+  // stage from reads of another), [waves][BYTES]
+  __shared__ __attribute__((aligned(1024))) char vst0[kWaves * TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vst1[kWaves * TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) char vst2[TL::STAGES == 3 ? kWaves * TL::BYTES : 1024];
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  char* vtiles = smem;                                     // [waves][2][BYTES]
-  int64_t* pre = (int64_t*)(smem + TL::REGION);            // [B + 1]
+  int64_t* pre = (int64_t*)(smem + TL::RED);               // [B + 1]
   int* lens_s = (int*)(pre + a.B + 1);                     // [B] clamped lengths
   __shared__ int64_t wsum[kWaves];
-  // wave partials for the combine, overlaid on the V tiles once a pass is done
+  // wave partials for the combine
   float* red_acc = (float*)smem;                           // [waves][kRows][D]
   float* red_m = red_acc + kWaves * kRows * D;             // [waves][kRows]
   float* red_l = red_m + kWaves * kRows;                   // [waves][kRows]
@@ -194,8 +202,26 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
   const int j = lane >> 4, i = lane & 15;  // lane quarter, lane in quarter
   const uint8_t* kb = (const uint8_t*)a.k;
   const uint8_t* vb = (const uint8_t*)a.v;
-  char* vt0 = vtiles + (2 * w) * TL::BYTES;
-  char* vt1 = vt0 + TL::BYTES;
+  // This lane's transposed V reads: byte offsets from a stage array, one per
+  // read group (16-dim block, or 32-dim int4 group).  Made opaque to the
+  // optimiser: every read address is then the stage array plus one register
+  // plus an immediate, which keeps the array's alias scope on the read (a
+  // deeper chain of address arithmetic loses it, and the wait counters would
+  // then hold the read until every copy in flight had landed).
+  constexpr int NVR = KV == ATTN_INT4 ? TL::CPR : TL::NDB;
+  int vro[NVR];
+#pragma unroll
+  for (int x = 0; x < NVR; ++x) {
+    if constexpr (KV == ATTN_BF16) {
+      const int col = 32 * x + 8 * (i & 3);  // byte within the row
+      const int r_lo = 8 * j + (i >> 2);
+      vro[x] = w * TL::BYTES + r_lo * TL::ROWB + 16 * ((col >> 4) ^ swz_v<KV, D>(r_lo)) + (col & 15);
+    } else {
+      const int rrow = 8 * j + (i >> 1);
+      vro[x] = w * TL::BYTES + rrow * TL::ROWB + 16 * (x ^ swz_v<KV, D>(rrow)) + 8 * (i & 1);
+    }
+    asm volatile("" : "+v"(vro[x]));
+  }
 
   // The split: segment (b, hk) occupies piece_groups charged slots followed
   // by its 16-token groups; all segments laid end to end (W slots) are cut
@@ -304,7 +330,8 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
         float4 vs4[8];        // int4: V scales of tokens 8j + e, all 4 groups
       };
       // loads of block starting at token g0: K operands to registers, V tile to LDS
-      auto issue = [&](int g0, Kbuf& kbf, char* vt) {
+      auto issue = [&](int g0, Kbuf& kbf, char* st) {
+        char* vt = st + w * TL::BYTES;
         const int tl = tend - 1;
         const int64_t base0 = page_row(__builtin_amdgcn_readfirstlane(min(g0, tl)));
         const int64_t base1 = page_row(__builtin_amdgcn_readfirstlane(min(g0 + 16, tl)));
@@ -375,34 +402,22 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
         bf16x8 v[TL::NDB];
         i32x2 raw4[TL::CPR];  // int4: 8 tokens x byte i of each 16-byte chunk (= 32-dim group)
       };
-      auto vread = [&](const char* vt, Vops& vo) {
+      auto vread = [&](char* st, Vops& vo) {
         bf16x8* vop = vo.v;
         if constexpr (KV == ATTN_INT4) {
 #pragma unroll
-          for (int c = 0; c < TL::CPR; ++c) {
-            const int rrow = 8 * j + (i >> 1);
-            const char* p = vt + rrow * TL::ROWB + 16 * (c ^ swz_v<KV, D>(rrow)) + 8 * (i & 1);
-            vo.raw4[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
-          }
+          for (int c = 0; c < TL::CPR; ++c) vo.raw4[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(st + vro[c]));
         } else if constexpr (KV == ATTN_BF16) {
 #pragma unroll
           for (int db = 0; db < TL::NDB; ++db) {
-            const int col = 32 * db + 8 * (i & 3);  // byte within the row
-            const int r_lo = 8 * j + (i >> 2), r_hi = r_lo + 4;
-            const char* p0 = vt + r_lo * TL::ROWB + 16 * ((col >> 4) ^ swz_v<KV, D>(r_lo)) + (col & 15);
-            const char* p1 = vt + r_hi * TL::ROWB + 16 * ((col >> 4) ^ swz_v<KV, D>(r_hi)) + (col & 15);
-            const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-            const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+            const i16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(st + vro[db]));
+            const i16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(st + vro[db] + 4 * TL::ROWB));
             vop[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
           }
         } else {
           i32x2 raw[TL::NDB];
 #pragma unroll
-          for (int db = 0; db < TL::NDB; ++db) {
-            const int rrow = 8 * j + (i >> 1);
-            const char* p = vt + rrow * TL::ROWB + 16 * (db ^ swz_v<KV, D>(rrow)) + 8 * (i & 1);
-            raw[db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)p);
-          }
+          for (int db = 0; db < TL::NDB; ++db) raw[db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(st + vro[db]));
 #pragma unroll
           for (int db = 0; db < TL::NDB; ++db) vop[db] = codes8_to_bf16<KV>((uint32_t)raw[db][0], (uint32_t)raw[db][1]);
         }
@@ -524,40 +539,88 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
         }
       };
 
-      // two-stage pipeline over this wave's blocks (every 4th 32-token block
-      // of [t0, tend)); counted, with a single loop exit
+      // pipeline over this wave's blocks (every 4th 32-token block of [t0, tend))
       const int nblk = tend > t0 ? (tend - t0 + kBlk - 1) / kBlk : 0;
       const int n_it = nblk > w ? (nblk - w + kWaves - 1) / kWaves : 0;
       constexpr int kStride = kWaves * kBlk;
-      int g0 = t0 + w * kBlk;
+      const int g0 = t0 + w * kBlk;
       // (the transposing V reads of a block come before the next block's
-      // direct-to-LDS copies: issued while copies are in flight, they would
-      // make the compiler wait for those copies first)
+      // direct-to-LDS copies into the same stage array would be issued)
       if (n_it > 0) {
-        Kbuf k0, k1;
         Vops vo;
-        issue(g0, k0, vt0);
-        int it = 0;
-        for (; it + 2 <= n_it; it += 2) {
-          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this block's loads have landed
-          vread(vt0, vo);
-          __builtin_amdgcn_sched_barrier(0);
-          issue(g0 + kStride, k1, vt1);
-          __builtin_amdgcn_sched_barrier(0);
-          consume(g0, k0, vo);
-          __builtin_amdgcn_s_waitcnt(0x0F70);
-          vread(vt1, vo);
-          __builtin_amdgcn_sched_barrier(0);
-          if (it + 2 < n_it) issue(g0 + 2 * kStride, k0, vt0);
-          __builtin_amdgcn_sched_barrier(0);
-          consume(g0 + kStride, k1, vo);
-          g0 += 2 * kStride;
+        if constexpr (TL::STAGES == 3) {
+          // Blocks it + 1 and it + 2 load while block it is consumed.  Every
+          // step issues one block, so every wait is the same count; blocks
+          // past the last are issued too (clamped onto the piece's last
+          // tokens: cached, valid data into stages nobody consumes).
+          constexpr int kWait = 0x0F70 | (TL::OPS & 15) | ((TL::OPS >> 4) << 14);  // vmcnt(OPS): one block may still load
+          static_assert(TL::OPS < 64, "wait count");
+          Kbuf k0, k1, k2;
+          issue(g0, k0, vst0);
+          issue(g0 + kStride, k1, vst1);
+          // full trips of three steps, no exit inside (an exit after a step
+          // would let the compiler sink the next blocks' K loads past it,
+          // behind later copies, and then wait for everything)
+          int it = 0, gi = g0;
+          for (; it + 3 <= n_it; it += 3, gi += 3 * kStride) {
+            __builtin_amdgcn_s_waitcnt(kWait);
+            vread(vst0, vo);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(gi + 2 * kStride, k2, vst2);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(gi, k0, vo);
+            __builtin_amdgcn_s_waitcnt(kWait);
+            vread(vst1, vo);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(gi + 3 * kStride, k0, vst0);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(gi + kStride, k1, vo);
+            __builtin_amdgcn_s_waitcnt(kWait);
+            vread(vst2, vo);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(gi + 4 * kStride, k1, vst1);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(gi + 2 * kStride, k2, vo);
+          }
+          // the last one or two blocks (already loading into stages 0 and 1)
+          if (it < n_it) {
+            __builtin_amdgcn_s_waitcnt(kWait);
+            vread(vst0, vo);
+            consume(gi, k0, vo);
+            if (it + 1 < n_it) {
+              __builtin_amdgcn_s_waitcnt(0x0F70);
+              vread(vst1, vo);
+              consume(gi + kStride, k1, vo);
+            }
+          }
+        } else {
+          // one block loads while the previous one is consumed (counted, with
+          // a single loop exit)
+          Kbuf k0, k1;
+          issue(g0, k0, vst0);
+          int it = 0, gi = g0;
+          for (; it + 2 <= n_it; it += 2) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this block's loads have landed
+            vread(vst0, vo);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(gi + kStride, k1, vst1);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(gi, k0, vo);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            vread(vst1, vo);
+            __builtin_amdgcn_sched_barrier(0);
+            if (it + 2 < n_it) issue(gi + 2 * kStride, k0, vst0);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(gi + kStride, k1, vo);
+            gi += 2 * kStride;
+          }
+          if (it < n_it) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            vread(vst0, vo);
+            consume(gi, k0, vo);
+          }
         }
-        if (it < n_it) {
-          __builtin_amdgcn_s_waitcnt(0x0F70);
-          vread(vt0, vo);
-          consume(g0, k0, vo);
-        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy into a V tile is still in flight
       }
 
       // the row's sum over the lane quarters; then combine the waves through LDS
@@ -568,7 +631,6 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
         lane_pair<32>(l, u0, u1);
         l = u0 + u1;
       }
-      __syncthreads();  // every wave is done with its V tiles (the partials overlay them)
 #pragma unroll
       for (int db = 0; db < TL::NDB; ++db)
 #pragma unroll
@@ -622,7 +684,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
         if (!whole) rec[(int64_t)RT * D + rg] = v;
         else if (a.lse) a.lse[((int64_t)b * a.Hq + (int64_t)hk * G + rg % G) * n_q + rg / G] = v * kLn2;
       }
-      __syncthreads();  // the partials are read before the next pass's copies land
+      __syncthreads();  // the partials are read before the next pass writes its own
     }
     if (tid == 0 && j0 == 0) {
       const int last = whole ? unit : (int)((seg_end * N - 1) / W);
@@ -635,7 +697,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
 
 template <int KV, int D>
 size_t mfma_lds_bytes(int B) {
-  return (size_t)MTile<KV, D>::REGION + (size_t)(B + 1) * sizeof(int64_t) + (size_t)B * sizeof(int);
+  return (size_t)MTile<KV, D>::RED + (size_t)(B + 1) * sizeof(int64_t) + (size_t)B * sizeof(int);
 }
 
 template <int KV, int D>

@@ -270,6 +270,30 @@ def test_decode_ragged_edge_cases(kv, paged, page_size, G, D, decode_path):
         check_lp(o, lse, ro, rl, f"{kv} paged={paged} ps={page_size} G={G} D={D} splits={ns}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "int8", "int4"])
+@pytest.mark.parametrize("n_q", [1, 3])
+@pytest.mark.parametrize("piece_bytes", [0, 1, 4096, 1 << 20, 1 << 26])
+def test_decode_piece_charge_in_split(kv, n_q, piece_bytes, monkeypatch):
+    """The matrix-core split charges each non-empty segment ATTN_DECODE_PIECE_BYTES worth of
+    slots before its groups: from no charge to charges far longer than the sequences (capped),
+    so that work units holding only charged slots, segments whose first group lies in a later
+    unit than their charge, and every remainder of the three-stage block pipeline occur.
+    Output == oracle for each charge and several unit counts."""
+    import oracle
+    monkeypatch.delenv("ATTN_DECODE_PATH", raising=False)
+    monkeypatch.setenv("ATTN_DECODE_PIECE_BYTES", str(piece_bytes))
+    lens = np.array([0, 1, 31, 33, 129, 640, 641, 1000, 2049, 5000], dtype=np.int32)
+    Hkv, G, D = 2, 4, 128
+    case = gen.decode_inputs(len(lens), G * Hkv, Hkv, D, lens, kv=kv, page_size=64, paged=True, spare=2,
+                             seed=500 + n_q, n_q=n_q if n_q > 1 else None)
+    ro, rl = oracle.decode(case)
+    for ns in (0, 2, 7, 64):
+        say(f"piece charge {piece_bytes} {kv} n_q={n_q} units={ns}")
+        o, lse = gpu_decode(case, num_splits=ns)
+        assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
+        check_lp(o, lse, ro, rl, f"piece charge {piece_bytes} {kv} n_q={n_q} units={ns}")
+
+
 def test_decode_many_sequences_mixed_lengths():
     """B=300 sequences (more than one length per thread of the on-chip prefix sum), with empty,
     tiny and long ones mixed, over 1, 7, automatic and more work units than token groups."""

@@ -142,6 +142,14 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len,
  *               read before being written.
  *   o           device [B, Hq, D] fp32 (written); lse device [B, Hq] fp32 or NULL.
  * A sequence with kv_lens[b] == 0 gets O = 0, lse = -inf.
+ * Tuning (environment, read at each call; results stay exact):
+ *   ATTN_DECODE_UNITS=n       automatic unit count n instead of one per CU;
+ *   ATTN_DECODE_PATH=valu     vector-ALU split kernel instead of the
+ *                             matrix-core one;
+ *   ATTN_DECODE_PIECE_BYTES=b the matrix-core split charges each non-empty
+ *                             (sequence, KV head) about b bytes of cache
+ *                             (default 144 KiB), the fixed cost of one more
+ *                             piece in a work unit.
  * Errors: ATTN_E_INVALID, ATTN_E_UNSUPPORTED (D, kv_dt, G > 8), ATTN_E_DEVICE.
  */
 attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, const void* k_cache, const void* v_cache,

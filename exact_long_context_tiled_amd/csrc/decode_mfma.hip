@@ -187,7 +187,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
   // stage from reads of another), [waves][BYTES]
   __shared__ __attribute__((aligned(1024))) char vst0[kWaves * TL::BYTES];
   __shared__ __attribute__((aligned(1024))) char vst1[kWaves * TL::BYTES];
-  __shared__ __attribute__((aligned(1024))) char vst2[TL::STAGES == 3 ? kWaves * TL::BYTES : 1024];
+  __shared__ __attribute__((aligned(16))) char vst2[TL::STAGES == 3 ? kWaves * TL::BYTES : 16];  // (unused with two stages)
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int64_t* pre = (int64_t*)(smem + TL::RED);               // [B + 1]
   int* lens_s = (int*)(pre + a.B + 1);                     // [B] clamped lengths

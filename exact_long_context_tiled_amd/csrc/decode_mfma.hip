@@ -19,21 +19,25 @@
 //                 accumulator of lane quarter j hold tokens 8j .. 8j+7 of the
 //                 block: the B operand of the next product as it stands.
 //   O^T += V^T P^T (16 dims x 16 rows, 32 tokens per product).  V goes
-//                 through LDS (direct global -> LDS copies into a per-wave
-//                 double buffer) and comes back transposed: two 16-bit
-//                 transposing reads (4 tokens each) for bf16, one 8-bit read
-//                 (8 tokens) for e4m3 / int8, converted exactly to bf16.
+//                 through LDS (direct global -> LDS copies into per-wave
+//                 tiles, two or three stages) and comes back transposed: two
+//                 16-bit transposing reads (4 tokens each) for bf16, one
+//                 8-bit read (8 tokens) for e4m3 / int8 / int4.
 //
 // e4m3 and int8 codes become exact bf16 numbers; P is rounded to bf16 as in
-// the prefill kernels.  int4 (32-element scale groups) is dequantised with its
-// scale into bf16 (rounded): a lane quarter of the K operand is exactly one
-// group of its token, and an 8-bit transposing V read gives a lane both
-// nibbles (two dims) of one byte column for 8 tokens, i.e. two A operands
-// (even and odd dims) whose 8 tokens carry that group's per-token scales.  int8 scales (per token) multiply the fp32 scores and
+// the prefill kernels.  int8 scales (per token) multiply the fp32 scores and
 // the softmax weights; e4m3 scales (per KV head) join scale*log2(e) and the
-// output factor.  Each of the 4 waves of a work-group scans every 4th
-// 32-token block of a piece with its own online softmax; the waves are then
-// combined through LDS and the piece's record (or the final output) written.
+// output factor.  int4 (32-element scale groups, D = 128) needs no
+// arithmetic per element: each code enters as the exact bf16 n + 136 (bit
+// masks), a transpose across lane quarters makes every k-step of S^T one
+// scale group (so a token's score is the sum of its group scales times the
+// group products), the V scales go into group-scaled copies of P, and
+// products with a constant -136 operand remove the offset.
+//
+// Each of the 4 waves of a work-group scans every 4th 32-token block of a
+// piece with its own online softmax; blocks load one (bf16) or two (smaller
+// tiles) ahead of the one consumed.  The waves are then combined through
+// LDS and the piece's record (or the final output) written.
 #include <math.h>
 #include <stdlib.h>
 

@@ -172,24 +172,22 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(PrefillArgs a
   float l = 0.f;        // this lane's half of the running sum
 
   // ---- direct global -> LDS copies of one K/V tile
+  // Copy c of wave w fills rows R*(4c + w) .. +R-1 of the tile (R rows per
+  // wave-wide copy).  Row r mod (chunks per row), which sets K's swizzle,
+  // and r mod 4, which sets V's, do not depend on c, so each lane has one
+  // byte offset for K and one for V, and the copies of a tile differ only by
+  // a scalar offset.  The copies go through buffer resources whose base moves
+  // with the tile (scalar registers), so the offsets are loop-invariant.
+  // Rows past the block are clamped onto the last key (finite data, masked
+  // below) on the one tile that reaches past it.
   const uint16_t* kbase = (const uint16_t*)a.k + b * a.k_sb + (int64_t)hk * D;
   const uint16_t* vbase = (const uint16_t*)a.v + b * a.k_sb + (int64_t)hk * D;
   const int cp_row = lane / TL::CPR;  // row within a copy
   const int cp_chunk = lane % TL::CPR;
-  // Copies go through buffer resources whose base moves with the tile (scalar
-  // registers), so the per-lane byte offsets below are loop-invariant.  V's
-  // swizzle does not depend on the copy index, so its copies differ only by a
-  // scalar offset.  Rows past the block are clamped onto the last key (finite
-  // data, masked below) on the one tile that reaches past it.
   const int ksb = (int)a.k_ss * 2;  // bytes between key rows (< 2^26)
-  uint32_t koff[TL::COPIES];
-#pragma unroll
-  for (int c = 0; c < TL::COPIES; ++c) {
-    const int rr = (w * TL::COPIES + c) * TL::ROWS_PER_COPY + cp_row;
-    koff[c] = (uint32_t)(rr * ksb + 16 * (cp_chunk ^ swz_k<D>(rr)));
-  }
-  const int rv0 = w * TL::COPIES * TL::ROWS_PER_COPY + cp_row;
-  const uint32_t voff = (uint32_t)(rv0 * ksb + 16 * (cp_chunk ^ swz_v<D>(rv0)));
+  const int r_w = w * TL::ROWS_PER_COPY + cp_row;  // this lane's row in copy 0
+  const uint32_t koff = (uint32_t)(r_w * ksb + 16 * (cp_chunk ^ swz_k<D>(r_w)));
+  const uint32_t voff = (uint32_t)(r_w * ksb + 16 * (cp_chunk ^ swz_v<D>(r_w)));
   auto issue_tile = [&](int t, char* kst) {
     char* vst = kst + TL::BYTES;
     const int64_t k0 = (int64_t)t * kBK;
@@ -197,36 +195,48 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(PrefillArgs a
     const int nrec = (int)(uint32_t)min(rem, (uint64_t)0xFFFFFFFFu);
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + k0 * a.k_ss), (short)0, nrec, kBufDword3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + k0 * a.k_ss), (short)0, nrec, kBufDword3);
+    // this wave's first copy within the stage; opaque, so each destination is
+    // formed here by one scalar add instead of being held in a register
+    int wo = w * 1024;
+    asm volatile("" : "+s"(wo));
     if (k0 + kBK <= a.n_k) {
 #pragma unroll
       for (int c = 0; c < TL::COPIES; ++c) {
-        const int q = w * TL::COPIES + c;  // copy index within the tile
-        copy16_to_lds(rk, (lds_void*)(kst + q * 1024), koff[c], 0);
-        copy16_to_lds(rv, (lds_void*)(vst + q * 1024), voff, c * TL::ROWS_PER_COPY * ksb);
+        const int so = c * kWaves * TL::ROWS_PER_COPY * ksb;
+        copy16_to_lds(rk, (lds_void*)(kst + wo + c * kWaves * 1024), koff, so);
+        copy16_to_lds(rv, (lds_void*)(vst + wo + c * kWaves * 1024), voff, so);
       }
     } else {
       const int last = (int)(a.n_k - 1 - k0);
 #pragma unroll
       for (int c = 0; c < TL::COPIES; ++c) {
-        const int q = w * TL::COPIES + c;
-        const int rr = q * TL::ROWS_PER_COPY + cp_row;
+        const int rr = (kWaves * c + w) * TL::ROWS_PER_COPY + cp_row;
         const int j = min(rr, last);
-        copy16_to_lds(rk, (lds_void*)(kst + q * 1024), (uint32_t)(j * ksb + 16 * (cp_chunk ^ swz_k<D>(rr))), 0);
-        copy16_to_lds(rv, (lds_void*)(vst + q * 1024), (uint32_t)(j * ksb + 16 * (cp_chunk ^ swz_v<D>(rr))), 0);
+        copy16_to_lds(rk, (lds_void*)(kst + wo + c * kWaves * 1024), (uint32_t)(j * ksb + 16 * (cp_chunk ^ swz_k<D>(rr))), 0);
+        copy16_to_lds(rv, (lds_void*)(vst + wo + c * kWaves * 1024), (uint32_t)(j * ksb + 16 * (cp_chunk ^ swz_v<D>(rr))), 0);
       }
     }
   };
 
   // V^T by transposed reads: lane (a=r16/4, b=r16%4) of each 16-lane group
   // addresses key row 8*(lane/32) + a (+4), columns 16*(g16%2) + 4*b
+  // (+ 32*db).  Rows 16c + v_row (+4) share v_row's swizzle, so the byte
+  // offset of block db from the stage is vofs[db] + 16c*ROWB (+ 4*ROWB).
+  // The offsets are opaque, so the reads keep their stage's alias scope.
   const int g16 = lane >> 4, r16 = lane & 15;
-  const int v_row = 8 * (g16 >> 1) + (r16 >> 2);       // + 16*c (+4)
-  const int v_col = 16 * (g16 & 1) + 4 * (r16 & 3);    // + 32*db (elements)
+  const int v_row = 8 * (g16 >> 1) + (r16 >> 2);
+  const int v_col = 16 * (g16 & 1) + 4 * (r16 & 3);
+  int vofs[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int col = 32 * db + v_col;
+    vofs[db] = TL::BYTES + v_row * TL::ROWB + 16 * ((col >> 3) ^ swz_v<D>(v_row)) + 2 * (col & 7);
+    asm volatile("" : "+v"(vofs[db]));
+  }
 
   auto tile_step = [&](int t, const char* Ks, char* next) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t have landed
     __syncthreads();                     // ... everyone's; and tile t-1 is fully consumed
-    const char* Vs = Ks + TL::BYTES;
     const int64_t k0 = (int64_t)t * kBK;
 
     // S^T = K Q^T, operands software-pipelined: the K chunks of step kk+1
@@ -259,12 +269,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(PrefillArgs a
 
     // V^T operand (key chunk c of 16, output rows 32*db ..) by two transposing reads
     auto vread = [&](int c, int db) {
-      const int row = 16 * c + v_row;
-      const int col = 32 * db + v_col;
-      const char* p0 = Vs + row * TL::ROWB + 16 * ((col >> 3) ^ swz_v<D>(row)) + 2 * (col & 7);
-      const char* p1 = p0 + 4 * TL::ROWB;  // row + 4 has the same swizzle
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+      const int o0 = vofs[db] + 16 * c * TL::ROWB;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Ks + o0));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Ks + o0 + 4 * TL::ROWB));
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     // all V^T operands of the tile, read before the next tile's copies are

@@ -34,6 +34,13 @@
 // group products), the V scales go into group-scaled copies of P, and
 // products with a constant -136 operand remove the offset.
 //
+// int8 and int4 scales of a block go through LDS with the V tile: one
+// wave-wide copy per block (4 bytes per lane for int8's per-token scales, 16
+// for int4's group scales), read back by each lane quarter for its 8 tokens.
+// Loaded per lane instead, every lane of a quarter would fetch the same
+// scales (16 extra loads per block for int4) and hold them in registers for
+// every pipeline stage.
+//
 // Each of the 4 waves of a work-group scans every 4th 32-token block of a
 // piece with its own online softmax; blocks load one (bf16) or two (smaller
 // tiles) ahead of the one consumed.  The waves are then combined through
@@ -64,7 +71,13 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 
+__device__ __forceinline__ void copy4_to_lds(const void* src, lds_void* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+#endif
+}
 __device__ __forceinline__ void copy16_to_lds(const void* src, lds_void* dst) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
@@ -169,7 +182,12 @@ struct MTile {
   static constexpr int STAGES = BYTES <= 4096 ? 3 : 2;
   // vector-memory operations of one block's loads (the fewest of their forms:
   // K operands, scales, V copies)
-  static constexpr int OPS = 2 * KL + COPIES + (KV == ATTN_INT8 ? 4 : KV == ATTN_INT4 ? 16 : 0);
+  static constexpr int OPS = 2 * KL + COPIES + (KV == ATTN_INT8 || KV == ATTN_INT4 ? 1 : 0);
+  // a wave's K and V scales of one block, staged in LDS after the V tiles of
+  // the stage: int8 one per token (32 x 2 floats), int4 one per 32-element
+  // group (32 x 4 x 2 floats)
+  static constexpr int SCB = KV == ATTN_INT4 ? 1024 : KV == ATTN_INT8 ? 256 : 0;
+  static constexpr int STAGE = kWaves * (BYTES + SCB);
   // wave partials of the combine (dynamic LDS, before the length prefix)
   static constexpr int RED = ((kWaves * kRows * D + 2 * kWaves * kRows) * 4 + 255) / 256 * 256;
 };
@@ -189,9 +207,9 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
   static_assert(KV != ATTN_INT4 || D == 128, "int4: one 32-element scale group per lane quarter");
   // V-tile stages, one array each (so the compiler tells copies into one
   // stage from reads of another), [waves][BYTES]
-  __shared__ __attribute__((aligned(1024))) char vst0[kWaves * TL::BYTES];
-  __shared__ __attribute__((aligned(1024))) char vst1[kWaves * TL::BYTES];
-  __shared__ __attribute__((aligned(16))) char vst2[TL::STAGES == 3 ? kWaves * TL::BYTES : 16];  // (unused with two stages)
+  __shared__ __attribute__((aligned(1024))) char vst0[TL::STAGE];
+  __shared__ __attribute__((aligned(1024))) char vst1[TL::STAGE];
+  __shared__ __attribute__((aligned(16))) char vst2[TL::STAGES == 3 ? TL::STAGE : 16];  // (unused with two stages)
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int64_t* pre = (int64_t*)(smem + TL::RED);               // [B + 1]
   int* lens_s = (int*)(pre + a.B + 1);                     // [B] clamped lengths
@@ -226,6 +244,10 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
     }
     asm volatile("" : "+v"(vro[x]));
   }
+  // this lane quarter's scales (tokens 8j .. 8j+7) in the wave's scale tile
+  // of a stage (opaque, like the V offsets)
+  int sro = kWaves * TL::BYTES + w * TL::SCB + TL::SCB / 8 * j;
+  asm volatile("" : "+v"(sro));
 
   // The split: segment (b, hk) occupies piece_groups charged slots followed
   // by its 16-token groups; all segments laid end to end (W slots) are cut
@@ -329,9 +351,6 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
       };
       struct Kbuf {
         uint4 k[2][TL::KL];
-        float4 ks[2], vs[2];  // int8: scales of tokens 8j .. 8j+7 of the block
-        float4 ks4[8];        // int4: K scales of tokens 8j + e, all 4 groups
-        float4 vs4[8];        // int4: V scales of tokens 8j + e, all 4 groups
       };
       // loads of block starting at token g0: K operands to registers, V tile to LDS
       auto issue = [&](int g0, Kbuf& kbf, char* st) {
@@ -348,48 +367,34 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
           for (int u = 0; u < TL::KL; ++u) kbf.k[sb][u] = src[u];
         }
         if constexpr (KV == ATTN_INT4) {
-          // K and V scales [row][4 groups] of tokens 8j .. 8j+7: aligned 16-byte loads
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int tk = min(g0 + 8 * j + e, tl);
+          // K and V scales [row][4 groups] of the block's 32 tokens into the
+          // wave's scale tile: K scales of token t at 16 t, V scales at
+          // 512 + 16 t.  One 16-byte copy per lane (lane L: token L % 32, K
+          // for L < 32), or four 4-byte copies when the scale arrays are not
+          // 16-byte aligned.
+          char* sct = st + kWaves * TL::BYTES + w * TL::SCB;
+          if (scales16) {
+            const int tk = min(g0 + (lane & 31), tl);
             const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
-            if (scales16) {
-              kbf.ks4[e] = *(const float4*)(a.k_scale + row * 4);
-              kbf.vs4[e] = *(const float4*)(a.v_scale + row * 4);
-            } else {
-              const float* kp = a.k_scale + row * 4;
-              const float* vp = a.v_scale + row * 4;
-              kbf.ks4[e] = float4{kp[0], kp[1], kp[2], kp[3]};
-              kbf.vs4[e] = float4{vp[0], vp[1], vp[2], vp[3]};
+            copy16_to_lds((lane < 32 ? a.k_scale : a.v_scale) + row * 4, (lds_void*)sct);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int o = 256 * q + 4 * lane;  // byte of the scale tile
+              const int tk = min(g0 + ((o & 511) >> 4), tl);
+              const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
+              copy4_to_lds((o < 512 ? a.k_scale : a.v_scale) + row * 4 + ((o & 15) >> 2), (lds_void*)(sct + 256 * q));
             }
           }
         }
         if constexpr (KV == ATTN_INT8) {
-          // the per-token scales of this lane quarter's 8 tokens (one 8-token run
-          // inside a page): two 16-byte loads each, or clamped single loads at the end
-          const int tb = g0 + 8 * j;
-          const int64_t base = (tb - g0 < 16 ? base0 : base1);
-          if (tb + 8 <= tend && scales16 && ((base + tb) & 3) == 0) {  // (16-byte aligned runs)
-            const float4* kp = (const float4*)(a.k_scale + base + tb);
-            const float4* vp = (const float4*)(a.v_scale + base + tb);
-            kbf.ks[0] = kp[0];
-            kbf.ks[1] = kp[1];
-            kbf.vs[0] = vp[0];
-            kbf.vs[1] = vp[1];
-          } else {
-            float kk[8], vv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int tk = min(tb + e, tl);
-              const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
-              kk[e] = a.k_scale[row];
-              vv[e] = a.v_scale[row];
-            }
-            kbf.ks[0] = float4{kk[0], kk[1], kk[2], kk[3]};
-            kbf.ks[1] = float4{kk[4], kk[5], kk[6], kk[7]};
-            kbf.vs[0] = float4{vv[0], vv[1], vv[2], vv[3]};
-            kbf.vs[1] = float4{vv[4], vv[5], vv[6], vv[7]};
-          }
+          // K and V scales of the block's 32 tokens into the wave's scale
+          // tile (K scale of token t at 4 t, V scale at 128 + 4 t): one
+          // 4-byte copy per lane (lane L: token L % 32, K for L < 32)
+          char* sct = st + kWaves * TL::BYTES + w * TL::SCB;
+          const int tk = min(g0 + (lane & 31), tl);
+          const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
+          copy4_to_lds((lane < 32 ? a.k_scale : a.v_scale) + row, (lds_void*)sct);
         }
 #pragma unroll
         for (int c = 0; c < TL::COPIES; ++c) {
@@ -405,12 +410,20 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
       struct Vops {
         bf16x8 v[TL::NDB];
         i32x2 raw4[TL::CPR];  // int4: 8 tokens x byte i of each 16-byte chunk (= 32-dim group)
+        f32x4 ks4[KV == ATTN_INT4 ? 8 : 1];  // int4: K scales of tokens 8j + e, all 4 groups
+        f32x4 vs4[KV == ATTN_INT4 ? 8 : 1];  // int4: V scales of tokens 8j + e, all 4 groups
+        f32x4 ks[2], vs[2];                  // int8: scales of tokens 8j .. 8j+7
       };
       auto vread = [&](char* st, Vops& vo) {
         bf16x8* vop = vo.v;
         if constexpr (KV == ATTN_INT4) {
 #pragma unroll
           for (int c = 0; c < TL::CPR; ++c) vo.raw4[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(st + vro[c]));
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            vo.ks4[e] = *(const lds_f32x4*)(st + sro + 16 * e);
+            vo.vs4[e] = *(const lds_f32x4*)(st + sro + 512 + 16 * e);
+          }
         } else if constexpr (KV == ATTN_BF16) {
 #pragma unroll
           for (int db = 0; db < TL::NDB; ++db) {
@@ -419,6 +432,12 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
             vop[db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
           }
         } else {
+          if constexpr (KV == ATTN_INT8) {
+            vo.ks[0] = *(const lds_f32x4*)(st + sro);
+            vo.ks[1] = *(const lds_f32x4*)(st + sro + 16);
+            vo.vs[0] = *(const lds_f32x4*)(st + sro + 128);
+            vo.vs[1] = *(const lds_f32x4*)(st + sro + 144);
+          }
           i32x2 raw[TL::NDB];
 #pragma unroll
           for (int db = 0; db < TL::NDB; ++db) raw[db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(st + vro[db]));
@@ -447,8 +466,8 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
             for (int ks = 0; ks < TL::NKS; ++ks) sg[ks] = mfma16(nib8_strided(d[ks]), qf[ks], qoff[ks]);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const float4 k4 = kbf.ks4[4 * sb + r];
-              sc[4 * sb + r] = k4.x * sg[0][r] + k4.y * sg[1][r] + k4.z * sg[2][r] + k4.w * sg[3][r];
+              const f32x4 k4 = vo.ks4[4 * sb + r];
+              sc[4 * sb + r] = k4[0] * sg[0][r] + k4[1] * sg[1][r] + k4[2] * sg[2][r] + k4[3] * sg[3][r];
             }
           }
         } else {
@@ -474,8 +493,8 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
         if constexpr (KV == ATTN_INT8) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            sc[e] *= kbf.ks[e >> 2][e & 3];
-            vsc[e] = kbf.vs[e >> 2][e & 3];
+            sc[e] *= vo.ks[e >> 2][e & 3];
+            vsc[e] = vo.vs[e >> 2][e & 3];
           }
         }
         if (g0 + kBlk > lim) {  // keys past this row's limit weigh nothing
@@ -528,7 +547,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
             constexpr int tok[8] = {0, 2, 1, 3, 4, 6, 5, 7};
             bf16x8 pc;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) pc[k] = (__bf16)(pv[tok[k]] * kbf.vs4[tok[k]][c]);
+            for (int k = 0; k < 8; ++k) pc[k] = (__bf16)(pv[tok[k]] * vo.vs4[tok[k]][c]);
             const uint32_t x0 = (uint32_t)vo.raw4[c][0] ^ kFlip8, x1 = (uint32_t)vo.raw4[c][1] ^ kFlip8;
             const bf16x8 lo8 = __builtin_bit_cast(bf16x8, uint4{nib_pair(x0, 0), nib_pair(x0, 8), nib_pair(x1, 0), nib_pair(x1, 8)});
             const bf16x8 hi8 = __builtin_bit_cast(bf16x8, uint4{nib_pair(x0, 4), nib_pair(x0, 12), nib_pair(x1, 4), nib_pair(x1, 12)});

@@ -330,11 +330,12 @@ def test_decode_multi_token_edge_cases(kv, G, n_q, D, decode_path):
             check_lp(o, lse, ro, rl, f"multi-token {kv} G={G} n_q={n_q} paged={paged} units={ns}")
 
 
-def test_decode_int8_scales_at_unaligned_addresses(decode_path):
-    """int8 scale arrays that start 4 bytes past a 16-byte boundary (read one by one)."""
+@pytest.mark.parametrize("kv", ["int8", "int4"])
+def test_decode_scales_at_unaligned_addresses(kv, decode_path):
+    """int8 / int4 scale arrays that start 4 bytes past a 16-byte boundary (copied in 4-byte pieces)."""
     import oracle
     lens = np.array([5, 40, 700], dtype=np.int32)
-    case = gen.decode_inputs(3, 8, 2, 128, lens, kv="int8", page_size=16, seed=91)
+    case = gen.decode_inputs(3, 8, 2, 128, lens, kv=kv, page_size=16, seed=91)
     ro, rl = oracle.decode(case)
     q = to_dev(case["q"])
     k, v = to_dev(case["k"]), to_dev(case["v"])
@@ -349,9 +350,9 @@ def test_decode_int8_scales_at_unaligned_addresses(decode_path):
     ks, vs = shifted(case["k_scale"]), shifted(case["v_scale"])
     assert ks.data_ptr() % 16 == 4
     o, lse = attn.decode_splitkv(q, k, v, lens_d, int(lens.max()), page_table=pt, k_scale=ks, v_scale=vs,
-                                 scale=case["scale"])
+                                 kv_dtype="int4" if kv == "int4" else None, scale=case["scale"])
     torch.cuda.synchronize()
-    check_lp(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, f"int8 unaligned scales {decode_path}")
+    check_lp(o.cpu().numpy(), lse.cpu().numpy(), ro, rl, f"{kv} unaligned scales {decode_path}")
 
 
 def test_decode_multi_one_token_is_splitkv():

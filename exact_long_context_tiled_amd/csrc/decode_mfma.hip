@@ -336,6 +336,11 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
         }
       }
       f32x4 acc[TL::NDB];
+      // int4: the -136 offset's share of group c's output, the same for its
+      // even and odd dims, added to both once the piece is scanned
+      f32x4 corr[KV == ATTN_INT4 ? TL::CPR : 1];
+#pragma unroll
+      for (int c = 0; c < (KV == ATTN_INT4 ? TL::CPR : 1); ++c) corr[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int db = 0; db < TL::NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
       float m = -INFINITY, l = 0.f;
@@ -519,6 +524,10 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
           l *= alpha;
 #pragma unroll
           for (int db = 0; db < TL::NDB; ++db) acc[db] *= alpha;
+          if constexpr (KV == ATTN_INT4) {
+#pragma unroll
+            for (int c = 0; c < TL::CPR; ++c) corr[c] *= alpha;
+          }
         }
         const float m_use = m == -INFINITY ? 0.f : m;
         bf16x8 pf;
@@ -539,7 +548,9 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
           // into acc[2c+1].  The codes enter as n + 136 (byte pairs 0, 2 and
           // 1, 3 of each dword: token order 0, 2, 1, 3, 4, 6, 5, 7 in both
           // operands), each token's V scale of group c goes into its weight,
-          // and a product with the constant -136 takes the offset off.
+          // and a product with the constant -136 (one per group: the even and
+          // odd dims share it, added to both after the scan) takes the offset
+          // off.
           const uint16_t cn = kBf16Neg136;
           const bf16x8 neg136 = __builtin_bit_cast(bf16x8, uint4{cn * 0x10001u, cn * 0x10001u, cn * 0x10001u, cn * 0x10001u});
 #pragma unroll
@@ -552,9 +563,8 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
             const bf16x8 lo8 = __builtin_bit_cast(bf16x8, uint4{nib_pair(x0, 0), nib_pair(x0, 8), nib_pair(x1, 0), nib_pair(x1, 8)});
             const bf16x8 hi8 = __builtin_bit_cast(bf16x8, uint4{nib_pair(x0, 4), nib_pair(x0, 12), nib_pair(x1, 4), nib_pair(x1, 12)});
             acc[2 * c] = mfma16(lo8, pc, acc[2 * c]);
-            acc[2 * c] = mfma16(neg136, pc, acc[2 * c]);
             acc[2 * c + 1] = mfma16(hi8, pc, acc[2 * c + 1]);
-            acc[2 * c + 1] = mfma16(neg136, pc, acc[2 * c + 1]);
+            corr[c] = mfma16(neg136, pc, corr[c]);
           }
         } else {
 #pragma unroll
@@ -646,6 +656,13 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
         __builtin_amdgcn_s_waitcnt(0x0F70);  // no copy into a V tile is still in flight
       }
 
+      if constexpr (KV == ATTN_INT4) {
+#pragma unroll
+        for (int c = 0; c < TL::CPR; ++c) {
+          acc[2 * c] += corr[c];
+          acc[2 * c + 1] += corr[c];
+        }
+      }
       // the row's sum over the lane quarters; then combine the waves through LDS
       {
         float u0, u1;

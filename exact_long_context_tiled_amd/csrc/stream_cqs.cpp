@@ -231,7 +231,7 @@ void for_task_pairs(const Geometry& g, int64_t i, F&& fn) {
 void cqs_count(CqsPlan& p, int B, int Hq, int Hkv, int64_t S, int64_t T, int D, int causal, attn_dtype dt) {
   const int64_t es = elem_size(dt);
   Geometry g{S, T, causal, &p};
-  std::vector<char> touched((size_t)p.n, 0);
+  std::vector<int64_t> writer((size_t)p.n, -1);  // sub-task that last wrote a block's running result
   std::vector<char> qin((size_t)p.k), kin((size_t)p.k);
   int64_t tasks = 0, pairs = 0, h2d = 0, d2h = 0;
   for (int64_t i = 0; i < p.n; ++i) {
@@ -252,9 +252,12 @@ void cqs_count(CqsPlan& p, int B, int Hq, int Hkv, int64_t S, int64_t T, int D, 
       if (!qin[a]) continue;
       const int64_t nq = g.q_rows(x);
       h2d += nq * Hq * D * es;
-      if (touched[(size_t)x]) h2d += nq * Hq * D * 4 + nq * Hq * 4;
+      // an earlier sub-task's running result comes back from the host, the
+      // previous sub-task's is copied on the device
+      const int64_t wr = writer[(size_t)x];
+      if (wr >= 0 && wr != tasks - 2) h2d += nq * Hq * D * 4 + nq * Hq * 4;
       d2h += nq * Hq * D * 4 + nq * Hq * 4;
-      touched[(size_t)x] = 1;
+      writer[(size_t)x] = tasks - 1;
     }
   }
   p.tasks = tasks * B;
@@ -384,7 +387,11 @@ extern "C" attn_status attn_stream_cqs(attn_dtype dt, const void* q_host, const 
   const int64_t K = p.k;
   char* arena = nullptr;
   float* lse_tmp = nullptr;  // pinned host lse when the caller passes none (running results need it)
-  hipStream_t s_in = nullptr, s_cmp = nullptr, s_out = nullptr;
+  // copy streams per direction.  Two measured slower than one on the 2^20-token
+  // workload (29-30 s against 20-22 s wall), so one it is; the scheduling
+  // below is written for any count.
+  constexpr int kCopyStreams = 1;
+  hipStream_t s_in[kCopyStreams] = {}, s_out[kCopyStreams] = {}, s_cmp = nullptr;
   std::vector<hipEvent_t> evs;
   std::vector<hipEvent_t> timing;
   attn_status result = ATTN_OK;
@@ -409,9 +416,11 @@ extern "C" attn_status attn_stream_cqs(attn_dtype dt, const void* q_host, const 
       ATTN_HIP(hipHostMalloc((void**)&lse_tmp, (size_t)B * Hq * S * 4, hipHostMallocDefault));
       lse_h = lse_tmp;
     }
-    ATTN_HIP(hipStreamCreateWithFlags(&s_in, hipStreamNonBlocking));
+    for (int c = 0; c < kCopyStreams; ++c) {
+      ATTN_HIP(hipStreamCreateWithFlags(&s_in[c], hipStreamNonBlocking));
+      ATTN_HIP(hipStreamCreateWithFlags(&s_out[c], hipStreamNonBlocking));
+    }
     ATTN_HIP(hipStreamCreateWithFlags(&s_cmp, hipStreamNonBlocking));
-    ATTN_HIP(hipStreamCreateWithFlags(&s_out, hipStreamNonBlocking));
     // slot s: K query-side blocks (Q, O, lse) then K key-side blocks (K, V)
     std::vector<char*> qbuf(2 * K), obuf(2 * K), lbuf(2 * K), kbuf(2 * K), vbuf(2 * K);
     {
@@ -425,12 +434,18 @@ extern "C" attn_status attn_stream_cqs(attn_dtype dt, const void* q_host, const 
           vbuf[s * K + a] = cur, cur += p.kv_bytes;
         }
     }
-    hipEvent_t ev_in[2], ev_done[2], ev_out[2];
+    // per slot: inbound copies landed (one per copy stream), compute done,
+    // write-back done (one per copy stream)
+    hipEvent_t ev_in[2][kCopyStreams], ev_done[2], ev_out[2][kCopyStreams];
     for (int s = 0; s < 2; ++s) {
-      ev_in[s] = ev(hipEventDisableTiming);
+      bool ok = true;
+      for (int c = 0; c < kCopyStreams; ++c) {
+        ev_in[s][c] = ev(hipEventDisableTiming);
+        ev_out[s][c] = ev(hipEventDisableTiming);
+        ok = ok && ev_in[s][c] && ev_out[s][c];
+      }
       ev_done[s] = ev(hipEventDisableTiming);
-      ev_out[s] = ev(hipEventDisableTiming);
-      if (!ev_in[s] || !ev_done[s] || !ev_out[s]) {
+      if (!ok || !ev_done[s]) {
         result = set_error(ATTN_E_DEVICE, "stream_cqs: event creation failed");
         goto done;
       }
@@ -446,6 +461,7 @@ extern "C" attn_status attn_stream_cqs(attn_dtype dt, const void* q_host, const 
     std::vector<Pair> prs;
     std::vector<char> qin((size_t)K), kin((size_t)K);
     int64_t job = 0;
+    int64_t prev_i = -1;  // quorum index of sub-task job - 1
     for (int64_t b = 0; b < B; ++b) {
       for (int64_t i = 0; i < p.n; ++i) {
         prs.clear();
@@ -460,25 +476,35 @@ extern "C" attn_status attn_stream_cqs(attn_dtype dt, const void* q_host, const 
         }
         int64_t* lw = &last_writer[(size_t)(b * p.n)];
         // ---- inbound: the slot is free once sub-task job-2 has written back
-        if (job >= 2) ATTN_HIP(hipStreamWaitEvent(s_in, ev_out[s], 0));
+        // (and after every inbound copy of the previous sub-task, on either
+        // stream: its device-to-device reads come from the slot written next)
+        for (int c = 0; c < kCopyStreams; ++c)
+          for (int c2 = 0; c2 < kCopyStreams; ++c2) {
+            if (job >= 2) ATTN_HIP(hipStreamWaitEvent(s_in[c], ev_out[s][c2], 0));
+            if (job >= 1) ATTN_HIP(hipStreamWaitEvent(s_in[c], ev_in[1 - s][c2], 0));
+          }
+        int ci = 0;  // inbound copies alternate between the copy streams
         for (int64_t a = 0; a < K; ++a) {
           const int64_t y = (p.base[(size_t)a] + i) % p.n;
           if (!kin[(size_t)a]) continue;
           const int64_t nk = g.k_rows(y);
           const size_t off = (size_t)((b * T + y * p.bk) * Hkv * D * es);
           ATTN_HIP(hipMemcpyAsync(kbuf[s * K + a], (const char*)k_host + off, nk * Hkv * D * es,
-                                  hipMemcpyHostToDevice, s_in));
+                                  hipMemcpyHostToDevice, s_in[ci++ % kCopyStreams]));
           ATTN_HIP(hipMemcpyAsync(vbuf[s * K + a], (const char*)v_host + off, nk * Hkv * D * es,
-                                  hipMemcpyHostToDevice, s_in));
+                                  hipMemcpyHostToDevice, s_in[ci++ % kCopyStreams]));
         }
-        // query blocks; running results of earlier sub-tasks, the previous sub-task's last
+        // query blocks; running results of earlier sub-tasks from the host, and
+        // those of the previous sub-task (consecutive quorums share a block)
+        // straight from its slot on the device: that needs only its compute,
+        // not its write-back, which then overlaps this sub-task
         for (int pass = 0; pass < 3; ++pass) {
           if (pass == 2) {
             bool any = false;
             for (int64_t a = 0; a < K; ++a)
               any |= qin[(size_t)a] && lw[(p.base[(size_t)a] + i) % p.n] == job - 1 && job >= 1;
             if (!any) break;
-            ATTN_HIP(hipStreamWaitEvent(s_in, ev_out[1 - s], 0));
+            for (int c = 0; c < kCopyStreams; ++c) ATTN_HIP(hipStreamWaitEvent(s_in[c], ev_done[1 - s], 0));
           }
           for (int64_t a = 0; a < K; ++a) {
             if (!qin[(size_t)a]) continue;
@@ -486,20 +512,39 @@ extern "C" attn_status attn_stream_cqs(attn_dtype dt, const void* q_host, const 
             const int64_t nq = g.q_rows(x), x0 = x * p.bq;
             if (pass == 0) {
               ATTN_HIP(hipMemcpyAsync(qbuf[s * K + a], (const char*)q_host + ((b * S + x0) * Hq * D) * es,
-                                      nq * Hq * D * es, hipMemcpyHostToDevice, s_in));
+                                      nq * Hq * D * es, hipMemcpyHostToDevice, s_in[ci++ % kCopyStreams]));
               continue;
             }
             const int64_t w = lw[x];
             if (w < 0 || (pass == 1) != (w < job - 1)) continue;
+            if (pass == 2) {
+              int64_t ap = -1;  // the block's place in the previous sub-task's quorum
+              for (int64_t c = 0; c < K; ++c)
+                if ((p.base[(size_t)c] + prev_i) % p.n == x) {
+                  ap = c;
+                  break;
+                }
+              if (ap < 0) {
+                result = set_error(ATTN_E_DEVICE, "stream_cqs: block %lld not in the previous quorum", (long long)x);
+                goto done;
+              }
+              hipStream_t sc = s_in[ci++ % kCopyStreams];
+              ATTN_HIP(hipMemcpyAsync(obuf[s * K + a], obuf[(1 - s) * K + ap], nq * Hq * D * 4,
+                                      hipMemcpyDeviceToDevice, sc));
+              ATTN_HIP(hipMemcpyAsync(lbuf[s * K + a], lbuf[(1 - s) * K + ap], nq * Hq * 4,
+                                      hipMemcpyDeviceToDevice, sc));
+              continue;
+            }
             ATTN_HIP(hipMemcpyAsync(obuf[s * K + a], (const char*)o_host + (b * S + x0) * Hq * D * 4,
-                                    nq * Hq * D * 4, hipMemcpyHostToDevice, s_in));
+                                    nq * Hq * D * 4, hipMemcpyHostToDevice, s_in[ci % kCopyStreams]));
             ATTN_HIP(hipMemcpy2DAsync(lbuf[s * K + a], (size_t)nq * 4, (const char*)lse_h + ((b * Hq) * S + x0) * 4,
-                                      (size_t)S * 4, (size_t)nq * 4, (size_t)Hq, hipMemcpyHostToDevice, s_in));
+                                      (size_t)S * 4, (size_t)nq * 4, (size_t)Hq, hipMemcpyHostToDevice,
+                                      s_in[ci++ % kCopyStreams]));
           }
         }
-        ATTN_HIP(hipEventRecord(ev_in[s], s_in));
+        for (int c = 0; c < kCopyStreams; ++c) ATTN_HIP(hipEventRecord(ev_in[s][c], s_in[c]));
         // ---- compute: one prefill launch per pair, merged into the query block's running result
-        ATTN_HIP(hipStreamWaitEvent(s_cmp, ev_in[s], 0));
+        for (int c = 0; c < kCopyStreams; ++c) ATTN_HIP(hipStreamWaitEvent(s_cmp, ev_in[s][c], 0));
         hipEvent_t t0 = ev(hipEventDefault), t1 = ev(hipEventDefault);
         if (!t0 || !t1) {
           result = set_error(ATTN_E_DEVICE, "stream_cqs: event creation failed");
@@ -533,24 +578,33 @@ extern "C" attn_status attn_stream_cqs(attn_dtype dt, const void* q_host, const 
         ATTN_HIP(hipEventRecord(t1, s_cmp));
         ATTN_HIP(hipEventRecord(ev_done[s], s_cmp));
         // ---- outbound: every query block this sub-task merged into
-        ATTN_HIP(hipStreamWaitEvent(s_out, ev_done[s], 0));
+        // (after the previous sub-task's write-back too: a block both wrote
+        // must reach the host in sub-task order)
+        for (int c = 0; c < kCopyStreams; ++c) {
+          ATTN_HIP(hipStreamWaitEvent(s_out[c], ev_done[s], 0));
+          if (job >= 1)
+            for (int c2 = 0; c2 < kCopyStreams; ++c2) ATTN_HIP(hipStreamWaitEvent(s_out[c], ev_out[1 - s][c2], 0));
+        }
+        int co = 0;
         for (int64_t a = 0; a < K; ++a) {
           if (!qin[(size_t)a]) continue;
           const int64_t x = (p.base[(size_t)a] + i) % p.n;
           const int64_t nq = g.q_rows(x), x0 = x * p.bq;
           ATTN_HIP(hipMemcpyAsync((char*)o_host + (b * S + x0) * Hq * D * 4, obuf[s * K + a], nq * Hq * D * 4,
-                                  hipMemcpyDeviceToHost, s_out));
+                                  hipMemcpyDeviceToHost, s_out[co % kCopyStreams]));
           ATTN_HIP(hipMemcpy2DAsync((char*)lse_h + ((b * Hq) * S + x0) * 4, (size_t)S * 4, lbuf[s * K + a],
-                                    (size_t)nq * 4, (size_t)nq * 4, (size_t)Hq, hipMemcpyDeviceToHost, s_out));
+                                    (size_t)nq * 4, (size_t)nq * 4, (size_t)Hq, hipMemcpyDeviceToHost,
+                                    s_out[co++ % kCopyStreams]));
           lw[x] = job;
         }
-        ATTN_HIP(hipEventRecord(ev_out[s], s_out));
+        for (int c = 0; c < kCopyStreams; ++c) ATTN_HIP(hipEventRecord(ev_out[s][c], s_out[c]));
+        prev_i = i;
         ++job;
       }
     }
-    ATTN_HIP(hipStreamSynchronize(s_in));
+    for (int c = 0; c < kCopyStreams; ++c) ATTN_HIP(hipStreamSynchronize(s_in[c]));
     ATTN_HIP(hipStreamSynchronize(s_cmp));
-    ATTN_HIP(hipStreamSynchronize(s_out));
+    for (int c = 0; c < kCopyStreams; ++c) ATTN_HIP(hipStreamSynchronize(s_out[c]));
     double ksum = 0.0;
     for (size_t t = 0; t + 1 < timing.size(); t += 2) {
       float ms = 0.f;
@@ -565,13 +619,17 @@ extern "C" attn_status attn_stream_cqs(attn_dtype dt, const void* q_host, const 
   }
 done:
 #undef ATTN_HIP
-  if (s_in) (void)hipStreamSynchronize(s_in);
+  for (int c = 0; c < kCopyStreams; ++c)
+    if (s_in[c]) (void)hipStreamSynchronize(s_in[c]);
   if (s_cmp) (void)hipStreamSynchronize(s_cmp);
-  if (s_out) (void)hipStreamSynchronize(s_out);
+  for (int c = 0; c < kCopyStreams; ++c)
+    if (s_out[c]) (void)hipStreamSynchronize(s_out[c]);
   for (hipEvent_t e : evs) (void)hipEventDestroy(e);
-  if (s_in) (void)hipStreamDestroy(s_in);
+  for (int c = 0; c < kCopyStreams; ++c) {
+    if (s_in[c]) (void)hipStreamDestroy(s_in[c]);
+    if (s_out[c]) (void)hipStreamDestroy(s_out[c]);
+  }
   if (s_cmp) (void)hipStreamDestroy(s_cmp);
-  if (s_out) (void)hipStreamDestroy(s_out);
   if (arena) (void)hipFree(arena);
   if (lse_tmp) (void)hipHostFree(lse_tmp);
   if (result == ATTN_OK && report)

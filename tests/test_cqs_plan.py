@@ -95,13 +95,14 @@ def _check_pairs(pairs, info, rep, S, T, causal, B):
 
 def _recount(pairs, info, rep, S, T, Hq, Hkv, D, es):
     """H2D / D2H bytes of executing the pair list: per sub-task, its key blocks
-    and query blocks go in, a query block's running (O, lse) goes in when an
-    earlier sub-task already wrote it, and every query block it touched goes out."""
+    and query blocks go in; a query block's running (O, lse) goes in when a
+    sub-task before the previous one wrote it last (the previous sub-task's
+    is copied on the device); every query block it touched goes out."""
     n = info["n_blocks"]
     bq, bk = rep["block_q"], rep["block_k"]
     h2d = d2h = 0
-    touched = set()
-    for (b, i), grp in itertools.groupby(pairs.tolist(), key=lambda r: (r[0], r[1])):
+    writer = {}  # (sequence, block) -> index of the sub-task that last wrote it
+    for t, ((b, i), grp) in enumerate(itertools.groupby(pairs.tolist(), key=lambda r: (r[0], r[1]))):
         grp = list(grp)
         xs = sorted({x for _, _, x, _ in grp})
         ys = sorted({y for _, _, _, y in grp if y >= 0})
@@ -110,10 +111,10 @@ def _recount(pairs, info, rep, S, T, Hq, Hkv, D, es):
         for x in xs:
             nq = min(S, (x + 1) * bq) - x * bq
             h2d += nq * Hq * D * es
-            if (b, x) in touched:
+            if writer.get((b, x), t - 1) < t - 1:
                 h2d += nq * Hq * (D + 1) * 4
             d2h += nq * Hq * (D + 1) * 4
-            touched.add((b, x))
+            writer[(b, x)] = t
     return h2d, d2h
 
 

@@ -475,14 +475,16 @@ extern "C" attn_status attn_stream_cqs(attn_dtype dt, const void* q_host, const 
           if (pr.b >= 0) kin[(size_t)pr.b] = 1;
         }
         int64_t* lw = &last_writer[(size_t)(b * p.n)];
-        // ---- inbound: the slot is free once sub-task job-2 has written back
-        // (and after every inbound copy of the previous sub-task, on either
-        // stream: its device-to-device reads come from the slot written next)
-        for (int c = 0; c < kCopyStreams; ++c)
-          for (int c2 = 0; c2 < kCopyStreams; ++c2) {
-            if (job >= 2) ATTN_HIP(hipStreamWaitEvent(s_in[c], ev_out[s][c2], 0));
+        // ---- inbound.  The slot's Q, K and V buffers are free once sub-task
+        // job-2 has computed; its O and lse buffers once that sub-task has
+        // written them back, so those copies come last.  (Every stream also
+        // follows every inbound copy of the previous sub-task: its
+        // device-to-device reads come from the slot written next.)
+        for (int c = 0; c < kCopyStreams; ++c) {
+          if (job >= 2) ATTN_HIP(hipStreamWaitEvent(s_in[c], ev_done[s], 0));
+          for (int c2 = 0; c2 < kCopyStreams; ++c2)
             if (job >= 1) ATTN_HIP(hipStreamWaitEvent(s_in[c], ev_in[1 - s][c2], 0));
-          }
+        }
         int ci = 0;  // inbound copies alternate between the copy streams
         for (int64_t a = 0; a < K; ++a) {
           const int64_t y = (p.base[(size_t)a] + i) % p.n;
@@ -499,6 +501,9 @@ extern "C" attn_status attn_stream_cqs(attn_dtype dt, const void* q_host, const 
         // straight from its slot on the device: that needs only its compute,
         // not its write-back, which then overlaps this sub-task
         for (int pass = 0; pass < 3; ++pass) {
+          if (pass == 1 && job >= 2)
+            for (int c = 0; c < kCopyStreams; ++c)
+              for (int c2 = 0; c2 < kCopyStreams; ++c2) ATTN_HIP(hipStreamWaitEvent(s_in[c], ev_out[s][c2], 0));
           if (pass == 2) {
             bool any = false;
             for (int64_t a = 0; a < K; ++a)

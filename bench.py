@@ -23,6 +23,13 @@ S=T=2^20, D=128, bf16, 4 GB device budget) from pinned host memory;
 ``--stream``, compares the two outputs).
 
 Prints ONE JSON line.  Inputs are seeded synthetic N(0,1) data.
+
+Each leg times ``--steps`` launches (default 50) after ``--warmup`` untimed
+ones (default 50).  After the GPU has been idle, the first few dozen
+back-to-back prefill launches run while its clock controller settles (on one
+box: 710 us, then up to 970 us, back to a steady 686-694 us from about the
+50th launch on, held over 400 launches); the warmup keeps that transient out
+of the timed region, so the figures are sustained rates.
 """
 from __future__ import annotations
 
@@ -438,8 +445,8 @@ def bench_stream(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")

@@ -82,9 +82,9 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(i32x2 raw) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// LDS tiles: kBK rows of D bytes, 16-byte chunks XOR-swizzled by the row
-// (chunk c of row r at c ^ (r mod chunks-per-row)), for both K (16 lanes read
-// one chunk of 16 rows) and V (16 lanes read 8 rows x 16 bytes).
+// LDS tiles: kBK rows of D bytes, 16-byte chunks XOR-swizzled by the row: V
+// by swz (chunk c of row r at c ^ (r mod chunks-per-row); 16 lanes read 8
+// rows x 16 bytes), K by swz_k below (16 lanes read one chunk of 16 rows).
 template <int D>
 struct Tile8 {
   static constexpr int ROWB = D;                  // bytes per row
@@ -97,6 +97,14 @@ struct Tile8 {
 template <int D>
 __device__ __forceinline__ int swz(int r) {
   return r & (D / 16 - 1);
+}
+// K tiles: chunk c of row r at c ^ ((r / (256 / row bytes)) mod chunks-per-row).
+// 16 lanes read one chunk of 16 rows; rows of D bytes start 256 / D rows
+// apart in bank order, so the swizzle must separate rows that agree mod
+// 256 / D (r mod chunks-per-row alone gives rows r and r + 8 the same banks).
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  return (r >> (D == 128 ? 1 : 2)) & (D / 16 - 1);
 }
 
 template <int D>
@@ -171,15 +179,19 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fp8_kernel(PrefillArgs a,
   const int cp_chunk = lane % TL::CPR;
   // Copies go through buffer resources whose base moves with the tile (scalar
   // registers); the per-lane byte offsets are loop-invariant.  The rows of
-  // one lane's copies differ by multiples of the chunks per row, so K and V
-  // share one swizzled chunk offset.  Rows past the block are clamped onto
-  // the last key (finite data, masked below): row offsets grow with the row,
-  // so the clamp is a min on the offset.
+  // one lane's copies differ by multiples of the chunks per row, so V needs
+  // one swizzled chunk offset and K (whose swizzle uses higher row bits) one
+  // per copy.  Rows past the block are clamped onto the last key (finite
+  // data, masked below): row offsets grow with the row, so the clamp is a min
+  // on the offset.
   const int ksb = (int)a.k_ss;  // bytes between key rows (< 2^24)
   int rowb[TL::COPIES];
 #pragma unroll
   for (int c = 0; c < TL::COPIES; ++c) rowb[c] = ((w * TL::COPIES + c) * TL::ROWS_PER_COPY + cp_row) * ksb;
-  const int chb = 16 * (cp_chunk ^ swz<D>(w * TL::COPIES * TL::ROWS_PER_COPY + cp_row));
+  const int chb = 16 * (cp_chunk ^ swz<D>(w * TL::COPIES * TL::ROWS_PER_COPY + cp_row));  // V
+  int chbk[TL::COPIES];                                                                    // K, per copy
+#pragma unroll
+  for (int c = 0; c < TL::COPIES; ++c) chbk[c] = 16 * (cp_chunk ^ swz_k<D>((w * TL::COPIES + c) * TL::ROWS_PER_COPY + cp_row));
   auto issue_tile = [&](int t, char* kst) {
     char* vst = kst + TL::BYTES;
     const int64_t k0 = (int64_t)t * kBK;
@@ -191,9 +203,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fp8_kernel(PrefillArgs a,
 #pragma unroll
     for (int c = 0; c < TL::COPIES; ++c) {
       const int q = w * TL::COPIES + c;
-      const uint32_t off = (uint32_t)(min(rowb[c], lastb) + chb);
-      copy16_to_lds(rk, (lds_void*)(kst + q * 1024), off);
-      copy16_to_lds(rv, (lds_void*)(vst + q * 1024), off);
+      const int rb = min(rowb[c], lastb);
+      copy16_to_lds(rk, (lds_void*)(kst + q * 1024), (uint32_t)(rb + chbk[c]));
+      copy16_to_lds(rv, (lds_void*)(vst + q * 1024), (uint32_t)(rb + chb));
     }
   };
 
@@ -212,7 +224,7 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fp8_kernel(PrefillArgs a,
 
     // S^T = K Q^T
     const int kr0 = perm_row(n);
-    const int ksw = swz<D>(kr0);  // the same swizzle for both blocks (32 = 0 mod chunks-per-row)
+    const int ksw = swz_k<D>(kr0);  // the same swizzle for both blocks (rows 32 apart)
     const char* krow = Ks + kr0 * TL::ROWB;
     auto kread = [&](int kk, int mb) {
       const char* base = krow + mb * 32 * TL::ROWB;

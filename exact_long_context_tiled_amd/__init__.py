@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     AttnError,
     decode_multi,
     decode_multi_workspace_size,
+    decode_set_tuning,
     decode_splitkv,
     decode_workspace_size,
     last_error,
@@ -32,6 +33,6 @@ from ._binding import (  # noqa: F401
 
 __all__ = [
     "AttnError", "prefill", "prefill_fp8", "decode_splitkv", "decode_workspace_size", "decode_multi",
-    "decode_multi_workspace_size", "merge_partials", "stream_budgeted",
+    "decode_multi_workspace_size", "decode_set_tuning", "merge_partials", "stream_budgeted",
     "stream_plan", "stream_cqs", "stream_cqs_plan", "last_error", "lib", "lib_path",
 ]

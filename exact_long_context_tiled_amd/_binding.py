@@ -79,6 +79,8 @@ def lib():
         L.attn_stream_cqs_plan.argtypes = [I, I, I, I, I64, I64, I, I, SZ, I64, P, I64, ctypes.POINTER(CqsInfo),
                                            ctypes.POINTER(StreamReport)]
         L.attn_stream_cqs_plan.restype = I
+        L.attn_decode_set_tuning.argtypes = [I, I, I64]
+        L.attn_decode_set_tuning.restype = I
         L.attn_last_error.argtypes = []
         L.attn_last_error.restype = ctypes.c_char_p
         _lib = L
@@ -150,6 +152,13 @@ def prefill_fp8(q, k, v, q_scale, k_scale, v_scale, *, causal=True, scale=None, 
     _check(lib().attn_prefill_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), B, Hq,
                                   Hkv, S, T, D, int(causal), scale, _ptr(out), _ptr(lse), _stream()))
     return out, lse
+
+
+def decode_set_tuning(*, path="auto", units=0, piece_bytes=-1):
+    """Process-wide decode tuning (attn_decode_set_tuning): path 'auto'
+    (matrix cores where supported) or 'valu'; units 0 = one per CU;
+    piece_bytes < 0 = the default charge per segment."""
+    _check(lib().attn_decode_set_tuning({"auto": 0, "valu": 1}[path], int(units), int(piece_bytes)))
 
 
 def decode_workspace_size(B, Hq, Hkv, D, max_kv_len, num_splits=0) -> int:

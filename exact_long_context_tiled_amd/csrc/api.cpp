@@ -54,13 +54,35 @@ attn_status raise_lds_limit(const void* kernel, size_t bytes, std::atomic<size_t
   return ATTN_OK;
 }
 
+namespace {
+std::atomic<int> g_dec_path{0}, g_dec_units{0};
+std::atomic<int64_t> g_dec_piece{-1};
+}  // namespace
+
+DecodeTuning decode_tuning() {
+  return DecodeTuning{g_dec_path.load(std::memory_order_relaxed), g_dec_units.load(std::memory_order_relaxed),
+                      g_dec_piece.load(std::memory_order_relaxed)};
+}
+
 }  // namespace attn
 
 using namespace attn;
 
+extern "C" attn_status attn_decode_set_tuning(int path, int units, int64_t piece_bytes) {
+  if (path != 0 && path != 1) return set_error(ATTN_E_INVALID, "decode tuning: path must be 0 or 1 (got %d)", path);
+  if (units < 0 || units > kDecodeMaxAutoUnits)
+    return set_error(ATTN_E_INVALID, "decode tuning: units must be in 0..%d (got %d)", kDecodeMaxAutoUnits, units);
+  g_dec_path.store(path, std::memory_order_relaxed);
+  g_dec_units.store(units, std::memory_order_relaxed);
+  g_dec_piece.store(piece_bytes < 0 ? -1 : piece_bytes, std::memory_order_relaxed);
+  return ATTN_OK;
+}
+
 extern "C" const char* attn_last_error(void) { return g_err; }
 
 namespace {
+
+bool aligned(const void* p, uintptr_t bytes) { return ((uintptr_t)p & (bytes - 1)) == 0; }
 
 // Arguments of a whole-sequence prefill ([B, S, Hq, D] queries against
 // [B, T, Hkv, D] keys); validation shared by the bf16 / fp32 and fp8 calls.
@@ -82,6 +104,10 @@ attn_status prefill_args(const char* what, const void* q, const void* k, const v
     return ATTN_OK;
   }
   if (!q || !o || (T > 0 && (!k || !v))) return set_error(ATTN_E_INVALID, "%s: null device pointer", what);
+  // 16-byte vector loads of Q, direct 16-byte copies of K/V, 16-byte O stores
+  if (!aligned(q, 16) || !aligned(o, 16) || (T > 0 && (!aligned(k, 16) || !aligned(v, 16))))
+    return set_error(ATTN_E_INVALID, "%s: q, k, v and o must be 16-byte aligned", what);
+  if (!aligned(lse, 4)) return set_error(ATTN_E_INVALID, "%s: lse must be 4-byte aligned", what);
   PrefillArgs a{};
   a.q = q;
   a.k = T > 0 ? k : q;
@@ -135,6 +161,8 @@ extern "C" attn_status attn_prefill_fp8(const void* q, const void* k, const void
   attn_status st = prefill_args("prefill_fp8", q, k, v, B, Hq, Hkv, S, T, D, causal, scale, o, lse, &a, &nothing);
   if (st != ATTN_OK || nothing) return st;
   if (!q_scale || !k_scale || !v_scale) return set_error(ATTN_E_INVALID, "prefill_fp8: null scale pointer");
+  if (!aligned(q_scale, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return set_error(ATTN_E_INVALID, "prefill_fp8: scales must be 4-byte aligned");
   a.q_scale = q_scale;
   a.k_scale = k_scale;
   a.v_scale = v_scale;
@@ -175,6 +203,12 @@ attn_status decode_impl(attn_dtype kv_dt, const void* q, const void* k_cache, co
   if (!q || !k_cache || !v_cache || !kv_lens || !o) return set_error(ATTN_E_INVALID, "decode: null device pointer");
   if (kv_dt != ATTN_BF16 && (!k_scale || !v_scale))
     return set_error(ATTN_E_INVALID, "decode: quantised KV needs k_scale and v_scale");
+  // 16-byte vector loads of q and of the caches
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return set_error(ATTN_E_INVALID, "decode: q, k_cache and v_cache must be 16-byte aligned");
+  if (!aligned(o, 4) || !aligned(lse, 4) || !aligned(kv_lens, 4) || !aligned(page_table, 4) ||
+      !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return set_error(ATTN_E_INVALID, "decode: o, lse, kv_lens, page_table and scales must be 4-byte aligned");
   int shift = 0;
   if (page_table) {
     if (page_size < 16 || (page_size & (page_size - 1)))
@@ -205,6 +239,7 @@ attn_status decode_impl(attn_dtype kv_dt, const void* q, const void* k_cache, co
   a.v_scale = v_scale;
   a.page_table = page_table;
   a.max_pages = max_pages;
+  a.num_pages = page_table ? num_pages : 0;
   a.page_size = page_size;
   a.page_shift = shift;
   a.kv_lens = kv_lens;
@@ -265,5 +300,7 @@ extern "C" attn_status attn_merge_partials(int n, const float* o_parts, const fl
   if (D < 1 || D > 1024) return set_error(ATTN_E_UNSUPPORTED, "merge: D must be in 1..1024 (got %d)", D);
   if (R == 0) return ATTN_OK;
   if (!o || (n > 0 && (!o_parts || !lse_parts))) return set_error(ATTN_E_INVALID, "merge: null device pointer");
+  if (!aligned(o, 4) || !aligned(lse, 4) || !aligned(o_parts, 4) || !aligned(lse_parts, 4))
+    return set_error(ATTN_E_INVALID, "merge: pointers must be 4-byte aligned");
   return launch_merge(n, o_parts, lse_parts, R, D, o, lse, (hipStream_t)stream);
 }

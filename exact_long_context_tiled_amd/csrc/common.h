@@ -80,6 +80,8 @@ struct DecodeArgs {
   const float* v_scale;
   const int32_t* page_table;  // null: contiguous
   int max_pages;
+  int num_pages;   // physical pages of a paged cache: entries outside [0, num_pages) are not
+                   // dereferenced (page 0 is read instead and the segment's rows come out NaN)
   int page_size;
   int page_shift;  // log2(page_size) when paged
   const int32_t* kv_lens;
@@ -114,6 +116,14 @@ inline int64_t decode_token_bytes(attn_dtype kv_dt, int D) {
     default: return 2 * (int64_t)D;                                 // e4m3 (per-head scales)
   }
 }
+// Process-wide decode tuning (attn_decode_set_tuning); results stay exact.
+struct DecodeTuning {
+  int path;             // 0: matrix cores where supported, 1: vector ALUs
+  int units;            // automatic unit count (0: one per compute unit)
+  int64_t piece_bytes;  // charge per non-empty segment in the matrix-core split (< 0: default)
+};
+constexpr int64_t kDecodePieceBytes = 144 << 10;
+DecodeTuning decode_tuning();
 // n_units == 0 picks one work-group per compute unit (at most
 // kDecodeMaxAutoUnits); the merge kernel runs after the split kernel.  The
 // split runs on the matrix cores for bf16 / e4m3 / int8 caches and D = 128

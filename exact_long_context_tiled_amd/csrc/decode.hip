@@ -235,6 +235,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
   __shared__ float red_acc[kDecodeWaves][RC * D];
   __shared__ float red_m[kDecodeWaves][RC], red_l[kDecodeWaves][RC];
   __shared__ int64_t wsum[kDecodeWaves];
+  __shared__ int red_bad[kDecodeWaves];  // per wave: a page-table entry outside the cache was met
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int slot = lane / LPT, part = lane % LPT;
@@ -279,6 +280,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
     if constexpr (KV == ATTN_FP8_E4M3) smul *= a.k_scale[hk];
     const int64_t hk_rows = (int64_t)hk * a.page_size;
     float* rec = a.part + (int64_t)(unit + seg) * REC;
+    bool bad_page = false;  // a page-table entry of this piece lay outside the cache
     for (int s0 = 0; s0 < n_q; s0 += TQ) {
     // query token s sits at position T - n_q + s and sees the keys before
     // T - (n_q - 1 - s); rows past the last query token repeat it (not written)
@@ -337,7 +339,12 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
         if (a.page_table) {
           // read through the constant address space: a scalar (SMEM) load
           const auto* pt = (const __attribute__((address_space(4))) int32_t*)a.page_table;
-          const int pg = pt[(int64_t)b * a.max_pages + (tc >> a.page_shift)];
+          const int pe = pt[(int64_t)b * a.max_pages + (tc >> a.page_shift)];
+          // an entry outside the cache is never dereferenced: page 0 is read
+          // instead and the rows of the piece are written as NaN
+          const bool ok = (uint32_t)pe < (uint32_t)a.num_pages;
+          bad_page |= !ok;
+          const int pg = ok ? pe : 0;
           step_row[u] = (int64_t)pg * a.Hkv * a.page_size + hk_rows - (tc & ~(a.page_size - 1));
         } else {
           step_row[u] = (int64_t)b * a.Hkv * a.page_size + hk_rows;
@@ -484,9 +491,13 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
         }
       }
     }
+    if (lane == 0) red_bad[w] = bad_page;
     __syncthreads();
     float vmul = 1.f;
     if constexpr (KV == ATTN_FP8_E4M3) vmul = a.v_scale[hk];
+    bool poison = false;
+#pragma unroll
+    for (int ww = 0; ww < kDecodeWaves; ++ww) poison |= red_bad[ww] != 0;
     // rows s0*G .. s0*G + RC - 1 of the segment's record; a row whose keys all
     // lie past its limit has a zero sum: O = 0, lse = -inf
     const int n_rows = tq_n * G;
@@ -502,7 +513,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
         num = fmaf(f, red_acc[ww][idx], num);
         den = fmaf(f, red_l[ww][g], den);
       }
-      const float val = den > 0.f ? num * (vmul / den) : 0.f;
+      const float val = poison ? __builtin_nanf("") : den > 0.f ? num * (vmul / den) : 0.f;
       if (whole) {  // o row (b, s0 + g / G, hk*G + g % G) of [B, n_q, Hq, D]
         const int64_t orow = ((int64_t)b * n_q + s0 + g / G) * a.Hq + (int64_t)hk * G + g % G;
         a.o[orow * D + idx % D] = val;
@@ -518,7 +529,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_split_kernel(DecodeArgs
 #pragma unroll
       for (int ww = 0; ww < kDecodeWaves; ++ww)
         den = fmaf(red_m[ww][tid] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(red_m[ww][tid] - M), red_l[ww][tid], den);
-      const float v = den > 0.f ? M + __log2f(den) : -INFINITY;
+      const float v = poison ? __builtin_nanf("") : den > 0.f ? M + __log2f(den) : -INFINITY;
       if (!whole) {
         rec[(int64_t)RT * D + s0 * G + tid] = v;
       } else if (a.lse) {  // lse [B, Hq, n_q]
@@ -566,48 +577,8 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a, int G) 
   if (n <= 1) return;
   const int RT = n_q * G;
   const int REC = decode_record_floats(RT, D);
-  const int r_rec = sq * G + g;  // the row's place in a record
-  const float* rec0 = a.part + (int64_t)first * REC;
-  float mx = -INFINITY, den = 0.f, acc[CPL];
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) acc[k] = 0.f;
-  // eight records at a time, all their loads issued before the first use;
-  // an online log-sum-exp update folds each batch in.  A record of a row
-  // that saw no key there has lse = -inf and weight 0.
-  for (int c0 = 0; c0 < n; c0 += 8) {
-    float lv[8], x[8][CPL];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float* rec = rec0 + (int64_t)min(c0 + r, n - 1) * REC;  // past the end: a valid record, weighted 0
-      lv[r] = rec[(int64_t)RT * D + r_rec];
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) x[r][k] = rec[(int64_t)r_rec * D + lane + 64 * k];
-    }
-    float bm = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      if (c0 + r >= n) lv[r] = -INFINITY;
-      bm = fmaxf(bm, lv[r]);
-    }
-    const float M = fmaxf(mx, bm);
-    if (M == -INFINITY) continue;  // nothing seen yet
-    const float f = __builtin_amdgcn_exp2f(mx - M);
-    den *= f;
-#pragma unroll
-    for (int k = 0; k < CPL; ++k) acc[k] *= f;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const float w = __builtin_amdgcn_exp2f(lv[r] - M);
-      den += w;
-#pragma unroll
-      for (int k = 0; k < CPL; ++k) acc[k] = fmaf(w, x[r][k], acc[k]);
-    }
-    mx = M;
-  }
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-#pragma unroll
-  for (int k = 0; k < CPL; ++k) orow[lane + 64 * k] = acc[k] * inv;
-  if (lane == 0 && a.lse) a.lse[lrow] = den > 0.f ? (mx + __log2f(den)) * kLn2 : -INFINITY;
+  dec::merge_row<D, false>(a.part + (int64_t)first * REC, REC, RT, sq * G + g, n, lane, orow,
+                           a.lse ? a.lse + lrow : nullptr);
 }
 
 template <int KV, int D, int G, int TQ>
@@ -670,15 +641,13 @@ size_t decode_workspace_bytes(int B, int Hkv, int rows, int D, int n_units_bound
 attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a0, int D, int G, hipStream_t stream) {
   DecodeArgs a = a0;
   a.G = G;
+  const DecodeTuning tu = decode_tuning();
   if (a.n_units <= 0) {
     // one work-group per compute unit: measured faster than filling every
     // resident slot (fewer partial records, and the scan stays bandwidth-bound)
-    a.n_units = std::min(kDecodeMaxAutoUnits, device_cu_count());
-    const char* env = getenv("ATTN_DECODE_UNITS");
-    if (env && atoi(env) > 0) a.n_units = std::min(kDecodeMaxAutoUnits, atoi(env));
+    a.n_units = std::min(kDecodeMaxAutoUnits, tu.units > 0 ? tu.units : device_cu_count());
   }
-  const char* path = getenv("ATTN_DECODE_PATH");
-  const bool valu = path && strcmp(path, "valu") == 0;
+  const bool valu = tu.path == 1;
   attn_status st;
   a.piece_groups = 0;
   if (decode_mfma_supported(kv_dt, D) && !valu) {
@@ -690,9 +659,7 @@ attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a0, int D, int G, 
     // correspondingly fewer keys, so work-groups with several pieces finish
     // with the others.
     const int64_t tok = decode_token_bytes(kv_dt, D) * kDecodeGroup;  // K + V bytes of one group, one KV head
-    int64_t cost = 144 << 10;
-    const char* env = getenv("ATTN_DECODE_PIECE_BYTES");
-    if (env && atoll(env) >= 0) cost = atoll(env);
+    const int64_t cost = tu.piece_bytes >= 0 ? tu.piece_bytes : kDecodePieceBytes;
     a.piece_groups = (int)std::min<int64_t>(kDecodeMaxPieceGroups, (cost + tok - 1) / tok);
     st = launch_decode_split_mfma(kv_dt, a, D, stream);
   } else {

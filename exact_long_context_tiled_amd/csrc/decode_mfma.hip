@@ -214,6 +214,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
   int64_t* pre = (int64_t*)(smem + TL::RED);               // [B + 1]
   int* lens_s = (int*)(pre + a.B + 1);                     // [B] clamped lengths
   __shared__ int64_t wsum[kWaves];
+  __shared__ int red_bad[kWaves];  // per wave: a page-table entry outside the cache was met
   // wave partials for the combine
   float* red_acc = (float*)smem;                           // [waves][kRows][D]
   float* red_m = red_acc + kWaves * kRows * D;             // [waves][kRows]
@@ -303,6 +304,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
     const int64_t hk_rows = (int64_t)hk * a.page_size;
     float* rec = a.part + (int64_t)(unit + seg) * REC;
 
+    bool bad_page = false;  // a page-table entry of this piece lay outside the cache
     for (int r0 = 0; r0 < RT; r0 += kRows) {
       const int n_rows = min(kRows, RT - r0);
       // this lane's row (clamped onto the pass's last row when past it: computed, not written)
@@ -349,7 +351,12 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
       auto page_row = [&](int t16) {  // first row of the 16-token group holding token t16 (wave-uniform)
         if (a.page_table) {
           const auto* pt = (const __attribute__((address_space(4))) int32_t*)a.page_table;
-          const int pg = pt[(int64_t)b * a.max_pages + (t16 >> a.page_shift)];
+          const int pe = pt[(int64_t)b * a.max_pages + (t16 >> a.page_shift)];
+          // an entry outside the cache is never dereferenced: page 0 is read
+          // instead and the rows of the piece are written as NaN
+          const bool ok = (uint32_t)pe < (uint32_t)a.num_pages;
+          bad_page |= !ok;
+          const int pg = ok ? pe : 0;
           return (int64_t)pg * a.Hkv * a.page_size + hk_rows - (t16 & ~(a.page_size - 1));
         }
         return (int64_t)b * a.Hkv * a.page_size + hk_rows;
@@ -530,7 +537,11 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
           }
         }
         const float m_use = m == -INFINITY ? 0.f : m;
-        bf16x8 pf;
+        // the weights as a bf16 pair hi + lo (lo = the rounding residue of
+        // hi): two P.V products carry them to ~2^-17 relative, where bf16
+        // alone would err by 2^-9 of each weight times |v|.  The scan is
+        // bound by HBM, so the second product is free.
+        bf16x8 pf, plo;
         float pv[8];
         float ls = 0.f;
 #pragma unroll
@@ -540,6 +551,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
           pv[e] = p;
           if constexpr (KV == ATTN_INT8) p = sc[e] == -INFINITY ? 0.f : p * vsc[e];
           pf[e] = (__bf16)p;
+          plo[e] = (__bf16)(p - (float)pf[e]);
         }
         l += ls;
         // O^T += V^T P^T
@@ -569,6 +581,8 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
         } else {
 #pragma unroll
           for (int db = 0; db < TL::NDB; ++db) acc[db] = mfma16(vop[db], pf, acc[db]);
+#pragma unroll
+          for (int db = 0; db < TL::NDB; ++db) acc[db] = mfma16(vop[db], plo, acc[db]);
         }
       };
 
@@ -684,9 +698,13 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
         red_m[w * kRows + i] = m;
         red_l[w * kRows + i] = l;
       }
+      if (lane == 0) red_bad[w] = bad_page;
       __syncthreads();
       float vmul = 1.f;
       if constexpr (KV == ATTN_FP8_E4M3) vmul = a.v_scale[hk];
+      bool poison = false;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) poison |= red_bad[ww] != 0;
       for (int idx = tid; idx < n_rows * D; idx += kThreads) {
         const int rr = idx / D, d = idx - rr * D;
         float M = red_m[rr];
@@ -700,7 +718,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
           num = fmaf(f, red_acc[(ww * kRows + rr) * D + d], num);
           den = fmaf(f, red_l[ww * kRows + rr], den);
         }
-        const float val = den > 0.f ? num * (vmul / den) : 0.f;
+        const float val = poison ? __builtin_nanf("") : den > 0.f ? num * (vmul / den) : 0.f;
         const int rg = r0 + rr;
         if (whole) {
           const int64_t orow = ((int64_t)b * n_q + rg / G) * a.Hq + (int64_t)hk * G + rg % G;
@@ -719,7 +737,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
           const float mw = red_m[ww * kRows + tid];
           den = fmaf(mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M), red_l[ww * kRows + tid], den);
         }
-        const float v = den > 0.f ? M + __log2f(den) : -INFINITY;
+        const float v = poison ? __builtin_nanf("") : den > 0.f ? M + __log2f(den) : -INFINITY;
         const int rg = r0 + tid;
         if (!whole) rec[(int64_t)RT * D + rg] = v;
         else if (a.lse) a.lse[((int64_t)b * a.Hq + (int64_t)hk * G + rg % G) * n_q + rg / G] = v * kLn2;

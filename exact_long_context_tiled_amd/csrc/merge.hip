@@ -49,10 +49,13 @@ __global__ void __launch_bounds__(256) merge_kernel(int n, const float* __restri
     if (tid == 0 && lse) lse[row] = -INFINITY;
     return;
   }
-  const int ng = D >= 256 ? 1 : 256 / D;      // column groups working on disjoint partials
-  const int grp = D >= 256 ? 0 : tid / D;
-  const int dl = D >= 256 ? tid : tid % D;
-  const bool active = grp < ng;
+  // Column groups working on disjoint partials: ng groups of D threads when
+  // D <= 128, else one group in which thread tid owns columns tid + 256k
+  // (for 128 < D < 256 the threads tid >= D own no column and stay idle).
+  const int ng = D > 128 ? 1 : 256 / D;
+  const int grp = D > 128 ? 0 : tid / D;
+  const int dl = D > 128 ? tid : tid % D;
+  const bool active = grp < ng && dl < D;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};  // D <= 1024 -> at most 4 columns per thread
   float den = 0.f;
   for (int c0 = 0; c0 < n; c0 += 256) {
@@ -89,7 +92,7 @@ __global__ void __launch_bounds__(256) merge_kernel(int n, const float* __restri
       for (int g = 0; g < ng; ++g) s += part[g * D + tid];
       orow[tid] = s * inv;
     }
-  } else {
+  } else if (active) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int d = dl + 256 * k;

@@ -30,6 +30,12 @@
  *  - Supported head dims: D = 64 or 128.  scale is explicit; callers
  *    usually pass 1/sqrt(D).
  *  - B == 0 or S == 0 (or R == 0) is a no-op returning ATTN_OK.
+ *  - Alignment: the kernels move data in 16-byte vectors, so the q, k, v and
+ *    o device pointers of the prefill calls, and the q, k_cache and v_cache
+ *    pointers of the decode calls, must be 16-byte aligned; every other
+ *    device pointer (fp32 outputs, scales, lse, page tables, lengths) needs
+ *    its natural 4-byte alignment.  A misaligned pointer is rejected with
+ *    ATTN_E_INVALID before anything is launched.
  */
 #ifndef ATTN_H
 #define ATTN_H
@@ -130,7 +136,10 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len,
  *   page_table  device int32 [B, max_pages]: physical page of logical page
  *               t / page_size of sequence b; entries past the sequence's
  *               last page are never read.  Paged mode needs page_size a power
- *               of two and a multiple of 16.
+ *               of two and a multiple of 16.  Every entry that is read must
+ *               lie in [0, num_pages): an entry outside it is not
+ *               dereferenced (the kernels read page 0 instead) and the output
+ *               rows and lse of that sequence come back NaN.
  *   kv_lens     device int32 [B]: tokens of each sequence (0..max_kv_len).
  *   max_kv_len  host int: upper bound of kv_lens (lengths are clamped to
  *               [0, max_kv_len]).
@@ -142,14 +151,7 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len,
  *               read before being written.
  *   o           device [B, Hq, D] fp32 (written); lse device [B, Hq] fp32 or NULL.
  * A sequence with kv_lens[b] == 0 gets O = 0, lse = -inf.
- * Tuning (environment, read at each call; results stay exact):
- *   ATTN_DECODE_UNITS=n       automatic unit count n instead of one per CU;
- *   ATTN_DECODE_PATH=valu     vector-ALU split kernel instead of the
- *                             matrix-core one;
- *   ATTN_DECODE_PIECE_BYTES=b the matrix-core split charges each non-empty
- *                             (sequence, KV head) about b bytes of cache
- *                             (default 144 KiB), the fixed cost of one more
- *                             piece in a work unit.
+ * Tuning: attn_decode_set_tuning below.
  * Errors: ATTN_E_INVALID, ATTN_E_UNSUPPORTED (D, kv_dt, G > 8), ATTN_E_DEVICE.
  */
 attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, const void* k_cache, const void* v_cache,
@@ -157,6 +159,21 @@ attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, const void* k_c
                                 int max_pages, int page_size, int num_pages, const int32_t* kv_lens,
                                 int max_kv_len, int B, int Hq, int Hkv, int D, float scale, int num_splits,
                                 void* workspace, size_t workspace_bytes, float* o, float* lse, void* stream);
+
+/*
+ * Process-wide tuning of attn_decode_splitkv / attn_decode_multi (results
+ * stay exact; the defaults are 0, 0, -1).  Thread-safe; a call already
+ * issued is not affected.
+ *   path         0 = matrix-core split kernel where it exists (bf16, e4m3 and
+ *                int8 caches, int4 with D = 128), 1 = vector-ALU split kernel
+ *   units        work units when num_splits == 0: 0 = one per compute unit,
+ *                else 1..2048
+ *   piece_bytes  the matrix-core split charges each non-empty (sequence, KV
+ *                head) about this many bytes of cache, the fixed cost of one
+ *                more piece in a work unit; < 0 = the default, 144 KiB
+ * Errors: ATTN_E_INVALID (path, units out of range).
+ */
+attn_status attn_decode_set_tuning(int path, int units, int64_t piece_bytes);
 
 /*
  * Workspace bytes attn_decode_multi needs for these sizes (num_splits as

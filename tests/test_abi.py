@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert set(syms) >= {"attn_prefill", "attn_decode_splitkv", "attn_merge_partials", "attn_stream_budgeted",
                          "attn_stream_plan", "attn_decode_workspace_size", "attn_last_error", "attn_stream_cqs",
                          "attn_stream_cqs_plan", "attn_decode_multi", "attn_decode_multi_workspace_size",
-                         "attn_prefill_fp8"}
+                         "attn_prefill_fp8", "attn_decode_set_tuning"}
     for s in syms:
         assert hasattr(L, s), s
 
@@ -226,3 +226,49 @@ def test_library_has_no_undefined_internal_symbols():
     out = subprocess.run([nm, "-C", "--undefined-only", attn.lib_path()], capture_output=True, text=True).stdout
     bad = [l for l in out.splitlines() if "attn::" in l]
     assert not bad, bad
+
+
+def test_misaligned_pointers_rejected_before_any_launch():
+    """The kernels move 16-byte vectors: misaligned device pointers are refused
+    with ATTN_E_INVALID by the argument checks, before anything is launched
+    (the fake addresses below are never dereferenced)."""
+    L = attn.lib()
+    A, M = 4096, 4096 + 4  # 16-byte aligned, and only 4-byte aligned
+    # prefill: q, k, v, o need 16 bytes
+    for q, k, v, o in ((M, A, A, A), (A, M, A, A), (A, A, M, A), (A, A, A, M)):
+        assert L.attn_prefill(1, q, k, v, 1, 4, 2, 8, 8, 64, 1, 0.1, o, None, None) == 1
+        assert "16-byte aligned" in attn.last_error()
+        assert L.attn_prefill_fp8(q, k, v, A, A, A, 1, 4, 2, 8, 8, 64, 1, 0.1, o, None, None) == 1
+    # lse needs 4 bytes
+    assert L.attn_prefill(1, A, A, A, 1, 4, 2, 8, 8, 64, 1, 0.1, A, A + 2, None) == 1
+    assert "4-byte" in attn.last_error()
+    # fp8 scales need 4 bytes
+    assert L.attn_prefill_fp8(A, A, A, A + 1, A, A, 1, 4, 2, 8, 8, 64, 1, 0.1, A, None, None) == 1
+    # decode: q and caches need 16 bytes, the rest 4
+    ws = 1 << 20
+    base = dict(q=A, k=A, v=A, ks=None, vs=None, pt=None, maxp=0, ps=512, npg=0, lens=A, maxlen=100, B=2, Hq=32,
+                Hkv=8, D=128, scale=0.1, ns=0, ws=1 << 24, wsb=ws, o=A, lse=None, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.attn_decode_splitkv(1, a["q"], a["k"], a["v"], a["ks"], a["vs"], a["pt"], a["maxp"], a["ps"],
+                                     a["npg"], a["lens"], a["maxlen"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                     a["scale"], a["ns"], a["ws"], a["wsb"], a["o"], a["lse"], a["st"])
+
+    for kw in (dict(q=M), dict(k=M), dict(v=M)):
+        assert call(**kw) == 1 and "16-byte aligned" in attn.last_error()
+    for kw in (dict(o=A + 2), dict(lse=A + 1), dict(lens=A + 2)):
+        assert call(**kw) == 1 and "4-byte aligned" in attn.last_error()
+    # merge: 4 bytes
+    assert L.attn_merge_partials(2, A + 1, A, 10, 64, A, None, None) == 1
+    assert L.attn_merge_partials(2, A, A, 10, 64, A + 3, None, None) == 1
+
+
+def test_decode_tuning_validation():
+    L = attn.lib()
+    assert L.attn_decode_set_tuning(2, 0, -1) == 1
+    assert L.attn_decode_set_tuning(0, -1, -1) == 1
+    assert L.attn_decode_set_tuning(0, 2049, -1) == 1
+    assert L.attn_decode_set_tuning(1, 64, 1 << 20) == 0
+    assert L.attn_decode_set_tuning(0, 0, -1) == 0
+

@@ -79,6 +79,10 @@ def lib():
         L.attn_stream_cqs_plan.argtypes = [I, I, I, I, I64, I64, I, I, SZ, I64, P, I64, ctypes.POINTER(CqsInfo),
                                            ctypes.POINTER(StreamReport)]
         L.attn_stream_cqs_plan.restype = I
+        L.attn_decode_splitkv_noalloc.argtypes = [I, P, P, P, P, P, P, I, I, I, P, I, I, I, I, I, F, I, P, P, P]
+        L.attn_decode_splitkv_noalloc.restype = I
+        L.attn_decode_noalloc_max_scratch.argtypes = []
+        L.attn_decode_noalloc_max_scratch.restype = SZ
         L.attn_decode_set_tuning.argtypes = [I, I, I64]
         L.attn_decode_set_tuning.restype = I
         L.attn_last_error.argtypes = []

@@ -6,6 +6,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace attn {
@@ -178,11 +180,42 @@ size_t decode_ws(int B, int Hq, int Hkv, int D, int n_q, int max_kv_len, int num
   return decode_workspace_bytes(B, Hkv, n_q * (Hq / Hkv), D, num_splits > 0 ? num_splits : kDecodeMaxAutoUnits);
 }
 
+// Scratch of the allocation-free decode entry point: a static device array
+// (one copy per GPU, resident for the life of the process), found per
+// device through hipGetSymbolAddress.  Host code never uses the array's name
+// as an address: that is a host-side stand-in.
+constexpr size_t kNoAllocScratchBytes = 8u << 20;
+static __device__ __attribute__((aligned(256))) char scratch[kNoAllocScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch` (looked up once per device).
+attn_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(ATTN_E_DEVICE, "decode_noalloc: cannot query the current device");
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p)
+        return set_error(ATTN_E_DEVICE, "decode_noalloc: no address for the scratch array: %s", hipGetErrorString(e));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return ATTN_OK;
+}
+
+// use_scratch: the workspace is the device's static scratch array (the
+// workspace arguments are ignored), for callers that cannot allocate.
 attn_status decode_impl(attn_dtype kv_dt, const void* q, const void* k_cache, const void* v_cache,
                         const float* k_scale, const float* v_scale, const int32_t* page_table, int max_pages,
                         int page_size, int num_pages, const int32_t* kv_lens, int max_kv_len, int B, int n_q, int Hq,
                         int Hkv, int D, float scale, int num_splits, void* workspace, size_t workspace_bytes,
-                        float* o, float* lse, void* stream) {
+                        float* o, float* lse, void* stream, bool use_scratch = false) {
   if (kv_dt != ATTN_BF16 && kv_dt != ATTN_INT8 && kv_dt != ATTN_FP8_E4M3 && kv_dt != ATTN_INT4)
     return set_error(ATTN_E_UNSUPPORTED, "decode: KV dtype must be bf16, int8, fp8 e4m3 or int4 (got %d)",
                      (int)kv_dt);
@@ -228,6 +261,15 @@ attn_status decode_impl(attn_dtype kv_dt, const void* q, const void* k_cache, co
   if (groups * (num_splits > 0 ? num_splits : kDecodeMaxAutoUnits) > 4e18)
     return set_error(ATTN_E_UNSUPPORTED, "decode: batch too large");
   const size_t need = decode_ws(B, Hq, Hkv, D, n_q, max_kv_len, num_splits);
+  if (use_scratch) {
+    if (need > kNoAllocScratchBytes)
+      return set_error(ATTN_E_UNSUPPORTED,
+                       "decode_noalloc: these sizes need %zu bytes of scratch; the static scratch holds %zu",
+                       need, kNoAllocScratchBytes);
+    attn_status st = scratch_of_current_device(&workspace);
+    if (st != ATTN_OK) return st;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (!workspace || workspace_bytes < need)
     return set_error(ATTN_E_INVALID, "decode: workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
   if (((uintptr_t)workspace) & 255) return set_error(ATTN_E_INVALID, "decode: workspace must be 256-byte aligned");
@@ -277,6 +319,18 @@ extern "C" attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, cons
                      kv_lens, max_kv_len, B, 1, Hq, Hkv, D, scale, num_splits, workspace, workspace_bytes, o, lse,
                      stream);
 }
+
+extern "C" attn_status attn_decode_splitkv_noalloc(attn_dtype kv_dt, const void* q, const void* k_cache,
+                                                   const void* v_cache, const float* k_scale, const float* v_scale,
+                                                   const int32_t* page_table, int max_pages, int page_size,
+                                                   int num_pages, const int32_t* kv_lens, int max_kv_len, int B,
+                                                   int Hq, int Hkv, int D, float scale, int num_splits, float* o,
+                                                   float* lse, void* stream) {
+  return decode_impl(kv_dt, q, k_cache, v_cache, k_scale, v_scale, page_table, max_pages, page_size, num_pages,
+                     kv_lens, max_kv_len, B, 1, Hq, Hkv, D, scale, num_splits, nullptr, 0, o, lse, stream, true);
+}
+
+extern "C" size_t attn_decode_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
 
 extern "C" size_t attn_decode_multi_workspace_size(int B, int n_q, int Hq, int Hkv, int D, int max_kv_len,
                                                    int num_splits) {

@@ -161,6 +161,29 @@ attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, const void* k_c
                                 void* workspace, size_t workspace_bytes, float* o, float* lse, void* stream);
 
 /*
+ * attn_decode_splitkv without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The partial records live in a static
+ * device array of attn_decode_noalloc_max_scratch() bytes (8 MiB), one copy
+ * per GPU, held until the process ends; the call allocates nothing.  Sizes
+ * whose workspace (attn_decode_workspace_size) would exceed it are rejected
+ * with ATTN_E_UNSUPPORTED.  Every call on one GPU shares that GPU's array, so
+ * calls that overlap on one GPU (on different streams, or from different
+ * threads without ordering) race and give wrong results.  Nothing in the array
+ * needs clearing: every record is written before it is read.
+ * Arguments and errors as attn_decode_splitkv; the first call on a device
+ * looks up the array's address (ATTN_E_DEVICE if that fails).
+ */
+attn_status attn_decode_splitkv_noalloc(attn_dtype kv_dt, const void* q, const void* k_cache, const void* v_cache,
+                                        const float* k_scale, const float* v_scale, const int32_t* page_table,
+                                        int max_pages, int page_size, int num_pages, const int32_t* kv_lens,
+                                        int max_kv_len, int B, int Hq, int Hkv, int D, float scale, int num_splits,
+                                        float* o, float* lse, void* stream);
+
+/* Bytes of the static scratch array of attn_decode_splitkv_noalloc. */
+size_t attn_decode_noalloc_max_scratch(void);
+
+/*
  * Process-wide tuning of attn_decode_splitkv / attn_decode_multi (results
  * stay exact; the defaults are 0, 0, -1).  Thread-safe; a call already
  * issued is not affected.

@@ -272,3 +272,21 @@ def test_decode_tuning_validation():
     assert L.attn_decode_set_tuning(1, 64, 1 << 20) == 0
     assert L.attn_decode_set_tuning(0, 0, -1) == 0
 
+
+def test_noalloc_decode_rejects_sizes_beyond_its_scratch():
+    """The allocation-free decode refuses, before touching a device, sizes whose
+    workspace exceeds its static scratch (addresses below are never dereferenced)."""
+    L = attn.lib()
+    cap = int(L.attn_decode_noalloc_max_scratch())
+    assert cap == 8 << 20
+    A = 4096
+    f = L.attn_decode_splitkv_noalloc
+    # B=4095 sequences x 8 KV heads x (4 rows x 128 + 16) floats per record: far beyond 8 MiB
+    assert attn.decode_workspace_size(4095, 32, 8, 128, 1000) > cap
+    assert f(1, A, A, A, None, None, None, 0, 1000, 0, A, 1000, 4095, 32, 8, 128, 0.1, 0, A, None, None) == 2
+    assert "scratch" in attn.last_error()
+    # validation still comes first
+    assert f(1, A, A, A, None, None, None, 0, 1000, 0, A, 1000, 2, 32, 8, 80, 0.1, 0, A, None, None) == 2
+    assert f(1, None, A, A, None, None, None, 0, 1000, 0, A, 1000, 2, 32, 8, 128, 0.1, 0, A, None, None) == 1
+    assert f(1, None, None, None, None, None, None, 0, 1000, 0, None, 1000, 0, 32, 8, 128, 0.1, 0, None, None,
+             None) == 0

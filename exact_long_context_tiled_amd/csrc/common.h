@@ -93,7 +93,10 @@ struct DecodeArgs {
   int piece_groups;  // groups each non-empty segment is charged in the split (matrix-core kernel; else 0)
   float scale_log2;
   float* part;       // records [N + B*Hkv - 1][R*D + pad16(R)], R = n_q*G: O rows, then lse (log2)
-  int32_t* seg_info; // [B*Hkv][2]: first record, record count (written by the segment's first unit)
+  int32_t* seg_info; // [B*Hkv][2]: vector-ALU split: first record, record count (written by the
+                     // segment's first unit); matrix-core split: one 64-bit arrival counter
+                     // per segment (tag << 16 | count) for its fused merge
+  uint64_t tag;      // per-call tag of the arrival counters (48 bits, nonzero)
   float* o;          // [B, n_q, Hq, D]
   float* lse;        // [B, Hq, n_q] or null
 };

@@ -661,7 +661,10 @@ attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a0, int D, int G, 
     const int64_t tok = decode_token_bytes(kv_dt, D) * kDecodeGroup;  // K + V bytes of one group, one KV head
     const int64_t cost = tu.piece_bytes >= 0 ? tu.piece_bytes : kDecodePieceBytes;
     a.piece_groups = (int)std::min<int64_t>(kDecodeMaxPieceGroups, (cost + tok - 1) / tok);
-    st = launch_decode_split_mfma(kv_dt, a, D, stream);
+    // the matrix-core split merges split segments itself (last-arriving unit)
+    static std::atomic<uint64_t> calls{0};
+    a.tag = (calls.fetch_add(1, std::memory_order_relaxed) % ((uint64_t(1) << 48) - 1)) + 1;
+    return launch_decode_split_mfma(kv_dt, a, D, stream);
   } else {
     switch (kv_dt) {
       case ATTN_BF16: st = launch_d<ATTN_BF16>(a, D, G, stream); break;

@@ -215,6 +215,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
   int* lens_s = (int*)(pre + a.B + 1);                     // [B] clamped lengths
   __shared__ int64_t wsum[kWaves];
   __shared__ int red_bad[kWaves];  // per wave: a page-table entry outside the cache was met
+  __shared__ int merge_first, merge_n;  // fused merge: first record and record count, or -1
   // wave partials for the combine
   float* red_acc = (float*)smem;                           // [waves][kRows][D]
   float* red_m = red_acc + kWaves * kRows * D;             // [waves][kRows]
@@ -257,6 +258,14 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
   const int64_t W = pre[a.B] * a.Hkv;
   const int64_t N = a.n_units < W ? (int64_t)a.n_units : W;
   const int unit = blockIdx.x;
+  // empty sequences: O = 0, lse = -inf (every launched work-group takes some)
+  for (int bb = unit; bb < a.B; bb += (int)gridDim.x) {
+    if (lens_s[bb] != 0) continue;
+    const int per_b = a.n_q * a.Hq;
+    for (int idx = tid; idx < per_b * D; idx += kThreads) a.o[(int64_t)bb * per_b * D + idx] = 0.f;
+    if (a.lse)
+      for (int idx = tid; idx < per_b; idx += kThreads) a.lse[(int64_t)bb * per_b + idx] = -INFINITY;
+  }
   if (unit >= N) return;
   // W = qd N + rw, so floor(u W / N) = u qd + floor(u rw / N), the last term
   // in 32 bits (u, rw < N <= 65535)
@@ -724,7 +733,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
           const int64_t orow = ((int64_t)b * n_q + rg / G) * a.Hq + (int64_t)hk * G + rg % G;
           a.o[orow * D + d] = val;
         } else {
-          rec[(int64_t)rg * D + d] = val;
+          dec::rec_store<true>(rec + (int64_t)rg * D + d, val);
         }
       }
       if (tid < n_rows) {
@@ -739,15 +748,49 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
         }
         const float v = poison ? __builtin_nanf("") : den > 0.f ? M + __log2f(den) : -INFINITY;
         const int rg = r0 + tid;
-        if (!whole) rec[(int64_t)RT * D + rg] = v;
+        if (!whole) dec::rec_store<true>(rec + (int64_t)RT * D + rg, v);
         else if (a.lse) a.lse[((int64_t)b * a.Hq + (int64_t)hk * G + rg % G) * n_q + rg / G] = v * kLn2;
       }
       __syncthreads();  // the partials are read before the next pass writes its own
     }
-    if (tid == 0 && j0 == 0) {
-      const int last = whole ? unit : (int)((seg_end * N - 1) / W);
-      a.seg_info[2 * seg] = unit + seg;
-      a.seg_info[2 * seg + 1] = last - unit + 1;
+    if (!whole) {
+      // Fused merge: the segment's records come from the units holding its
+      // groups, fu .. lu (records fu + seg .. lu + seg).  Each such unit
+      // counts itself in at device scope once its record stores (device
+      // scope too) have completed; the one that completes the count merges
+      // the records into the output and clears the counter for the next call.
+      // The counter word holds a 48-bit per-call tag above a 16-bit count, so
+      // a word left from an earlier call or never written counts as zero.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0) {
+        const int64_t fu = ((gstart + 1) * N - 1) / W;
+        const int64_t lu = (seg_end * N - 1) / W;
+        const uint64_t nrec = (uint64_t)(lu - fu + 1);
+        uint64_t* ctr = (uint64_t*)a.seg_info + seg;
+        uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint64_t nw;
+        do {
+          nw = (old >> 16) == a.tag ? old + 1 : (a.tag << 16) | 1;
+        } while (!__hip_atomic_compare_exchange_weak(ctr, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+        const bool last = (nw & 0xFFFF) == nrec;
+        if (last) __hip_atomic_store(ctr, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        merge_first = last ? (int)(fu + seg) : -1;
+        merge_n = (int)nrec;
+      }
+      __syncthreads();
+      asm volatile("" ::: "memory");
+      const int first = merge_first, n_rec = merge_n;
+      if (first >= 0) {
+        for (int rr = w; rr < RT; rr += kWaves) {
+          const int sq = rr / G, g = rr - (rr / G) * G;
+          const int h = hk * G + g;
+          float* orow = a.o + (((int64_t)b * n_q + sq) * a.Hq + h) * D;
+          float* lse_out = a.lse ? a.lse + ((int64_t)b * a.Hq + h) * n_q + sq : nullptr;
+          dec::merge_row<D, true>(a.part + (int64_t)first * REC, REC, RT, rr, n_rec, lane, orow, lse_out);
+        }
+      }
     }
     pos = pend;
   }

@@ -147,8 +147,12 @@ size_t attn_decode_workspace_size(int B, int Hq, int Hkv, int D, int max_kv_len,
  *               2048), else the number of work units (<= 65535) the batch's
  *               KV is divided into.  B <= 4095.
  *   workspace   device, >= attn_decode_workspace_size(...) bytes, 256-byte
- *               aligned; scratch for the partials, owned by the caller, not
- *               read before being written.
+ *               aligned; scratch for the partials, owned by the caller.  Its
+ *               contents need no initialisation: the partial records are
+ *               written before they are read, and the per-segment arrival
+ *               counters of the fused merge carry a per-call tag (a word
+ *               from another call, or never written, counts as zero; the
+ *               call leaves them cleared).
  *   o           device [B, Hq, D] fp32 (written); lse device [B, Hq] fp32 or NULL.
  * A sequence with kv_lens[b] == 0 gets O = 0, lse = -inf.
  * Tuning: attn_decode_set_tuning below.
@@ -170,7 +174,8 @@ attn_status attn_decode_splitkv(attn_dtype kv_dt, const void* q, const void* k_c
  * with ATTN_E_UNSUPPORTED.  Every call on one GPU shares that GPU's array, so
  * calls that overlap on one GPU (on different streams, or from different
  * threads without ordering) race and give wrong results.  Nothing in the array
- * needs clearing: every record is written before it is read.
+ * needs clearing: every record is written before it is read, and the fused
+ * merge's arrival counters carry a per-call tag (see workspace above).
  * Arguments and errors as attn_decode_splitkv; the first call on a device
  * looks up the array's address (ATTN_E_DEVICE if that fails).
  */

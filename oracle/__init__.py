@@ -56,6 +56,8 @@ def load():
         lib.oracle_bf16_value.restype = ctypes.c_double
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -149,6 +151,11 @@ def e4m3fn_value(code: int) -> float:
 def threads() -> int:
     """OpenMP threads the oracle uses."""
     return load().oracle_threads()
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of later oracle calls (timing only; results do not depend on it)."""
+    load().oracle_set_threads(int(n))
 
 
 def bf16_value(bits: int) -> float:

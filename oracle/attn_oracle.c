@@ -56,6 +56,16 @@ int oracle_threads(void) {
 #endif
 }
 
+/* Sets the threads of later calls (n >= 1); only the timing of the oracle
+   changes, every row is computed the same way on any thread. */
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8_E4M3 = 2, OR_INT8 = 3, OR_INT4 = 4 };
 
 enum { OR_INT4_GROUP = 32 }; /* elements per int4 scale group */

@@ -692,3 +692,51 @@ def test_stream_cqs_empty_keys_and_errors():
     with pytest.raises(attn.AttnError) as e:
         attn.stream_cqs(qh, kh, vh, causal=True, budget=4096)
     assert e.value.status == 3 and torch.cuda.mem_get_info()[0] == free0
+
+
+# ------------------------------------------------------------------ graph replay
+@pytest.mark.parametrize("kv", ["bf16", "int8"])
+def test_decode_graph_replay_matches_eager(kv):
+    """Split-KV decode captured in a HIP graph and replayed several times, with eager
+    work and synchronisations between the replays: every replay equals the eager call
+    bit for bit (the fused merge's arrival counters are cleared by each call, so a
+    replay with the same per-call tag starts from zero)."""
+    lens = np.array([700, 1500, 33, 4000], dtype=np.int32)
+    case = gen.decode_inputs(4, 32, 8, 128, lens, kv=kv, page_size=512, seed=71)
+    q = to_dev(case["q"])
+    k, v = to_dev(case["k"], kv), to_dev(case["v"], kv)
+    ks = to_dev(case["k_scale"]) if case.get("k_scale") is not None else None
+    vs = to_dev(case["v_scale"]) if case.get("v_scale") is not None else None
+    pt = to_dev(case["page_table"])
+    lens_d = to_dev(lens)
+    maxlen = int(lens.max())
+    ws = torch.empty(attn.decode_workspace_size(4, 32, 8, 128, maxlen), dtype=torch.uint8, device="cuda")
+    o = torch.empty((4, 32, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((4, 32), dtype=torch.float32, device="cuda")
+
+    def call():
+        attn.decode_splitkv(q, k, v, lens_d, maxlen, page_table=pt, k_scale=ks, v_scale=vs, scale=case["scale"],
+                            workspace=ws, out=o, lse=lse)
+
+    call()
+    torch.cuda.synchronize()
+    ref_o, ref_l = o.clone(), lse.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm the side stream (LDS limits are raised outside the capture)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        o.zero_()
+        lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"graph replay {rep} {kv}")
+        assert torch.equal(o, ref_o) and torch.equal(lse, ref_l), rep
+        call()  # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o)

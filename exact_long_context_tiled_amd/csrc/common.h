@@ -128,9 +128,11 @@ struct DecodeTuning {
 constexpr int64_t kDecodePieceBytes = 144 << 10;
 DecodeTuning decode_tuning();
 // n_units == 0 picks one work-group per compute unit (at most
-// kDecodeMaxAutoUnits); the merge kernel runs after the split kernel.  The
-// split runs on the matrix cores for bf16 / e4m3 / int8 caches and D = 128
-// int4 caches (unless ATTN_DECODE_PATH=valu), on the vector ALUs otherwise.
+// kDecodeMaxAutoUnits).  The split runs on the matrix cores for bf16 / e4m3 /
+// int8 caches and D = 128 int4 caches (unless the tuning selects the vector
+// ALUs), on the vector ALUs otherwise.  The matrix-core split merges its own
+// segments in the same launch; the vector-ALU split is followed by the merge
+// kernel.
 attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a, int D, int G, hipStream_t stream);
 bool decode_mfma_supported(attn_dtype kv_dt, int D);
 attn_status launch_decode_split_mfma(attn_dtype kv_dt, const DecodeArgs& a, int D, hipStream_t stream);

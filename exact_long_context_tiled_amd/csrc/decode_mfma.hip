@@ -124,18 +124,24 @@ __device__ __forceinline__ bf16x8 codes8_to_bf16(uint32_t w0, uint32_t w1) {
 // bf16 bit pattern 0x4300 | v is the value 128 + v = n + 136 (exponent 2^7,
 // v in the low mantissa bits).  The offset 136 is taken off afterwards by a
 // product with the constant operand kNeg136 below.
-constexpr uint32_t kNibMask2 = 0x000F000Fu;
-constexpr uint32_t kMagic2 = 0x43004300u;
-constexpr uint32_t kFlip8 = 0x88888888u;
 constexpr uint16_t kBf16Neg136 = 0xC308u;
 
-__device__ __forceinline__ uint32_t nib_pair(uint32_t x, int sh) { return ((x >> sh) & kNibMask2) | kMagic2; }
+// Codes e and e + 4 of x >> sh (bits sh .. sh+3 and sh+16 .. sh+19) as the
+// bf16 pair n + 136.  One three-input bit operation per word: where
+// kNibBits is set the result is the code bit XOR kNibSet (which flips bit 3
+// of each code: code ^ 8 = n + 8), elsewhere it is kNibSet (the 0x4300
+// exponent pattern).  The truth table 0x6A is f(a, b, c) = b ? a ^ c : c
+// evaluated on the operand masks a = 0xF0, b = 0xCC, c = 0xAA.
+constexpr uint32_t kNibBits = 0x000F000Fu;
+constexpr uint32_t kNibSet = 0x43084308u;
+__device__ __forceinline__ uint32_t nib_pair(uint32_t x, int sh) {
+  return __builtin_amdgcn_bitop3_b32(x >> sh, kNibBits, kNibSet, 0x6A);
+}
 
 // The 8 codes of w (code e at bits 4e .. 4e+3), as n + 136, in the element
 // order 0, 4, 1, 5, 2, 6, 3, 7 (nib_pair of a shift takes codes e and e + 4).
 __device__ __forceinline__ bf16x8 nib8_strided(uint32_t w) {
-  const uint32_t x = w ^ kFlip8;
-  return __builtin_bit_cast(bf16x8, uint4{nib_pair(x, 0), nib_pair(x, 4), nib_pair(x, 8), nib_pair(x, 12)});
+  return __builtin_bit_cast(bf16x8, uint4{nib_pair(w, 0), nib_pair(w, 4), nib_pair(w, 8), nib_pair(w, 12)});
 }
 
 // 4x4 transpose of dwords across the lane quarters: lane (j, i) holds d[c]
@@ -373,17 +379,38 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
       struct Kbuf {
         uint4 k[2][TL::KL];
       };
-      // loads of block starting at token g0: K operands to registers, V tile to LDS
+      // Block addresses.  A 32-token block starts on a 16-token group, so
+      // each of its halves lies within one page: the block's two half bases
+      // are wave-uniform (scalar), and each lane adds an offset of its own.
+      // The K loads of lanes i >= 8 lie in the second half; V copy c lies in
+      // half c / (COPIES / 2).  Tokens past the piece are clamped onto its
+      // last token (cached, valid data, never weighed); on the last block a
+      // clamped token of the second half lies in the first half's group, and
+      // then both half bases are that group's.  The clamp is branch-free, so
+      // every block issues the same instructions (a branch around the loads
+      // would make the compiler drain the loads in flight at every step).
+      const bool k_hi = i >= 8;
+      int ktok[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) ktok[sb] = 8 * (i >> 2) + 4 * sb + (i & 3);
+      constexpr int kRowsPerCopy = 1024 / TL::ROWB;
+      const int v_rr0 = 16 * lane / TL::ROWB;
+      const uint32_t vcol = (uint32_t)(16 * (((16 * lane) % TL::ROWB / 16) ^ swz_v<KV, D>(v_rr0)));
+      // loads of the block starting at token g0: K operands to registers, V
+      // tile (and int8 / int4 scales) to LDS
       auto issue = [&](int g0, Kbuf& kbf, char* st) {
         char* vt = st + w * TL::BYTES;
         const int tl = tend - 1;
-        const int64_t base0 = page_row(__builtin_amdgcn_readfirstlane(min(g0, tl)));
-        const int64_t base1 = page_row(__builtin_amdgcn_readfirstlane(min(g0 + 16, tl)));
+        // A block wholly past the piece (issued ahead, never consumed) is
+        // moved onto its last token, so every in-block offset stays >= 0.
+        const int gb = min(g0, tl);
+        const int lim = tl - gb;  // the last in-block token that is loaded as itself
+        const int64_t row0 = page_row(__builtin_amdgcn_readfirstlane(gb)) + gb;
+        const int64_t row1 = page_row(__builtin_amdgcn_readfirstlane(min(g0 + 16, tl))) + gb;
+        const uint8_t* kp = k_hi ? kb + row1 * TL::ROWB : kb + row0 * TL::ROWB;
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-          const int tk = min(g0 + 8 * (i >> 2) + 4 * sb + (i & 3), tl);
-          const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
-          const uint4* src = (const uint4*)(kb + row * TL::ROWB + TL::QB * j);
+          const uint4* src = (const uint4*)(kp + (uint32_t)(min(ktok[sb], lim) * TL::ROWB + TL::QB * j));
 #pragma unroll
           for (int u = 0; u < TL::KL; ++u) kbf.k[sb][u] = src[u];
         }
@@ -395,16 +422,16 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
           // 16-byte aligned.
           char* sct = st + kWaves * TL::BYTES + w * TL::SCB;
           if (scales16) {
-            const int tk = min(g0 + (lane & 31), tl);
-            const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
-            copy16_to_lds((lane < 32 ? a.k_scale : a.v_scale) + row * 4, (lds_void*)sct);
+            const int ts = lane & 31;
+            const float* arr = lane < 32 ? a.k_scale : a.v_scale;
+            copy16_to_lds(arr + ((ts >= 16 ? row1 : row0) + min(ts, lim)) * 4, (lds_void*)sct);
           } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int o = 256 * q + 4 * lane;  // byte of the scale tile
-              const int tk = min(g0 + ((o & 511) >> 4), tl);
-              const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
-              copy4_to_lds((o < 512 ? a.k_scale : a.v_scale) + row * 4 + ((o & 15) >> 2), (lds_void*)(sct + 256 * q));
+              const int ts = (o & 511) >> 4;
+              const float* arr = o < 512 ? a.k_scale : a.v_scale;
+              copy4_to_lds(arr + ((ts >= 16 ? row1 : row0) + min(ts, lim)) * 4 + ((o & 15) >> 2), (lds_void*)(sct + 256 * q));
             }
           }
         }
@@ -413,18 +440,15 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
           // tile (K scale of token t at 4 t, V scale at 128 + 4 t): one
           // 4-byte copy per lane (lane L: token L % 32, K for L < 32)
           char* sct = st + kWaves * TL::BYTES + w * TL::SCB;
-          const int tk = min(g0 + (lane & 31), tl);
-          const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
-          copy4_to_lds((lane < 32 ? a.k_scale : a.v_scale) + row, (lds_void*)sct);
+          const int ts = lane & 31;
+          const float* arr = lane < 32 ? a.k_scale : a.v_scale;
+          copy4_to_lds(arr + (ts >= 16 ? row1 : row0) + min(ts, lim), (lds_void*)sct);
         }
 #pragma unroll
         for (int c = 0; c < TL::COPIES; ++c) {
-          const int off = c * 1024 + 16 * lane;
-          const int rr = off / TL::ROWB;
-          const int pch = (off % TL::ROWB) / 16;
-          const int tk = min(g0 + rr, tl);
-          const int64_t row = (tk - g0 < 16 ? base0 : base1) + tk;
-          copy16_to_lds(vb + row * TL::ROWB + 16 * (pch ^ swz_v<KV, D>(rr)), (lds_void*)(vt + c * 1024));
+          const uint8_t* vp = vb + (c < TL::COPIES / 2 ? row0 : row1) * TL::ROWB;
+          const int rr = min(c * kRowsPerCopy + v_rr0, lim);
+          copy16_to_lds(vp + (uint32_t)(rr * TL::ROWB + vcol), (lds_void*)(vt + c * 1024));
         }
       };
       // V^T operands of a block: lane (j, i) holds dim 16*db + i of tokens 8j .. 8j+7
@@ -580,7 +604,7 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
             bf16x8 pc;
 #pragma unroll
             for (int k = 0; k < 8; ++k) pc[k] = (__bf16)(pv[tok[k]] * vo.vs4[tok[k]][c]);
-            const uint32_t x0 = (uint32_t)vo.raw4[c][0] ^ kFlip8, x1 = (uint32_t)vo.raw4[c][1] ^ kFlip8;
+            const uint32_t x0 = (uint32_t)vo.raw4[c][0], x1 = (uint32_t)vo.raw4[c][1];
             const bf16x8 lo8 = __builtin_bit_cast(bf16x8, uint4{nib_pair(x0, 0), nib_pair(x0, 8), nib_pair(x1, 0), nib_pair(x1, 8)});
             const bf16x8 hi8 = __builtin_bit_cast(bf16x8, uint4{nib_pair(x0, 4), nib_pair(x0, 12), nib_pair(x1, 4), nib_pair(x1, 12)});
             acc[2 * c] = mfma16(lo8, pc, acc[2 * c]);

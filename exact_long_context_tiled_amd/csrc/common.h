@@ -125,7 +125,7 @@ struct DecodeTuning {
   int units;            // automatic unit count (0: one per compute unit)
   int64_t piece_bytes;  // charge per non-empty segment in the matrix-core split (< 0: default)
 };
-constexpr int64_t kDecodePieceBytes = 144 << 10;
+constexpr int64_t kDecodePieceBytes = 192 << 10;
 DecodeTuning decode_tuning();
 // n_units == 0 picks one work-group per compute unit (at most
 // kDecodeMaxAutoUnits).  The split runs on the matrix cores for bf16 / e4m3 /

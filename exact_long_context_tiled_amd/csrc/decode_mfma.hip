@@ -738,26 +738,33 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
       bool poison = false;
 #pragma unroll
       for (int ww = 0; ww < kWaves; ++ww) poison |= red_bad[ww] != 0;
-      for (int idx = tid; idx < n_rows * D; idx += kThreads) {
-        const int rr = idx / D, d = idx - rr * D;
-        float M = red_m[rr];
-#pragma unroll
-        for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, red_m[ww * kRows + rr]);
-        float num = 0.f, den = 0.f;
+      // four consecutive dims of one row per item: the row's wave weights
+      // once, then one 16-byte LDS read per wave
+      for (int idx = tid; idx < n_rows * (D / 4); idx += kThreads) {
+        const int rr = idx / (D / 4), d0 = 4 * (idx - rr * (D / 4));
+        float mw[kWaves];
+        float M = -INFINITY;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
-          const float mw = red_m[ww * kRows + rr];
-          const float f = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-          num = fmaf(f, red_acc[(ww * kRows + rr) * D + d], num);
-          den = fmaf(f, red_l[ww * kRows + rr], den);
+          mw[ww] = red_m[ww * kRows + rr];
+          M = fmaxf(M, mw[ww]);
         }
-        const float val = poison ? __builtin_nanf("") : den > 0.f ? num * (vmul / den) : 0.f;
+        float den = 0.f;
+        f32x4 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+          const float f = mw[ww] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[ww] - M);
+          den = fmaf(f, red_l[ww * kRows + rr], den);
+          num += f * *(const f32x4*)(red_acc + (ww * kRows + rr) * D + d0);
+        }
+        const float sc = den > 0.f ? vmul / den : 0.f;
         const int rg = r0 + rr;
-        if (whole) {
-          const int64_t orow = ((int64_t)b * n_q + rg / G) * a.Hq + (int64_t)hk * G + rg % G;
-          a.o[orow * D + d] = val;
-        } else {
-          dec::rec_store<true>(rec + (int64_t)rg * D + d, val);
+        const int64_t orow = ((int64_t)b * n_q + rg / G) * a.Hq + (int64_t)hk * G + rg % G;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float val = poison ? __builtin_nanf("") : num[e] * sc;
+          if (whole) a.o[orow * D + d0 + e] = val;
+          else dec::rec_store<true>(rec + (int64_t)rg * D + d0 + e, val);
         }
       }
       if (tid < n_rows) {

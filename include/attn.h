@@ -198,7 +198,7 @@ size_t attn_decode_noalloc_max_scratch(void);
  *                else 1..2048
  *   piece_bytes  the matrix-core split charges each non-empty (sequence, KV
  *                head) about this many bytes of cache, the fixed cost of one
- *                more piece in a work unit; < 0 = the default, 144 KiB
+ *                more piece in a work unit; < 0 = the default, 192 KiB
  * Errors: ATTN_E_INVALID (path, units out of range).
  */
 attn_status attn_decode_set_tuning(int path, int units, int64_t piece_bytes);

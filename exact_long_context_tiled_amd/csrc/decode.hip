@@ -654,7 +654,7 @@ attn_status launch_decode(attn_dtype kv_dt, const DecodeArgs& a0, int D, int G, 
     // Each piece of a run (a segment, or the part of one inside the run) has
     // a fixed cost on the matrix-core kernel: its pipeline start, the wave
     // combine and the record, ~6 us measured, about what one work-group
-    // streams in that time (~144 KB).  Charging every segment that many
+    // streams in that time (192 KB by a sweep).  Charging every segment that many
     // groups in the split gives a run that reaches into another segment
     // correspondingly fewer keys, so work-groups with several pieces finish
     // with the others.

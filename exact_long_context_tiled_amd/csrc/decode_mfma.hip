@@ -318,6 +318,16 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
     if constexpr (KV == ATTN_FP8_E4M3) smul *= a.k_scale[hk];
     const int64_t hk_rows = (int64_t)hk * a.page_size;
     float* rec = a.part + (int64_t)(unit + seg) * REC;
+    // A split segment's counter word is brought to this call's tag with a
+    // count of zero as the launch starts, by each unit whose run begins in
+    // the segment (every split segment has one: all its units but the
+    // first).  A device-scope max leaves a word that already carries this
+    // call's tag, and any count in it, as it is, and nothing waits for it;
+    // the units finishing later then count themselves in with one add.  (A
+    // unit's later pieces do not open their segment: under full load the
+    // atomic's latency held up their first blocks.)
+    if (!whole && pos == x0 && tid == 0)
+      __hip_atomic_fetch_max((uint64_t*)a.seg_info + seg, a.tag << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     bool bad_page = false;  // a page-table entry of this piece lay outside the cache
     for (int r0 = 0; r0 < RT; r0 += kRows) {
@@ -795,17 +805,34 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (tid == 0) {
+        uint64_t* ctr = (uint64_t*)a.seg_info + seg;
+        // One device-scope add counts this unit in when the word carries
+        // this call's tag (raised at the pieces' start).  A word with a later
+        // tag (never written: any bits) is opened here for this call with a
+        // count of one, unless another unit has opened it meanwhile; the add
+        // has left its count meaningless.
+        const uint64_t v = __hip_atomic_fetch_add(ctr, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int64_t fu = ((gstart + 1) * N - 1) / W;
         const int64_t lu = (seg_end * N - 1) / W;
         const uint64_t nrec = (uint64_t)(lu - fu + 1);
-        uint64_t* ctr = (uint64_t*)a.seg_info + seg;
-        uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        uint64_t nw;
-        do {
-          nw = (old >> 16) == a.tag ? old + 1 : (a.tag << 16) | 1;
-        } while (!__hip_atomic_compare_exchange_weak(ctr, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT));
-        const bool last = (nw & 0xFFFF) == nrec;
+        uint64_t cnt;
+        if ((v >> 16) == a.tag) {
+          cnt = (v & 0xFFFF) + 1;
+        } else {
+          uint64_t old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          for (;;) {
+            if ((old >> 16) == a.tag) {
+              cnt = (__hip_atomic_fetch_add(ctr, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xFFFF) + 1;
+              break;
+            }
+            if (__hip_atomic_compare_exchange_weak(ctr, &old, (a.tag << 16) | 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)) {
+              cnt = 1;
+              break;
+            }
+          }
+        }
+        const bool last = cnt == nrec;
         if (last) __hip_atomic_store(ctr, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         merge_first = last ? (int)(fu + seg) : -1;
         merge_n = (int)nrec;

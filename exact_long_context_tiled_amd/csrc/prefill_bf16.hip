@@ -24,6 +24,8 @@
 //                   registers 0-7 / 8-15 of a lane hold 8 consecutive keys.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace attn {
@@ -234,20 +236,18 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(PrefillArgs a
     asm volatile("" : "+v"(vofs[db]));
   }
 
-  auto tile_step = [&](int t, const char* Ks, char* next) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t have landed
-    __syncthreads();                     // ... everyone's; and tile t-1 is fully consumed
-    const int64_t k0 = (int64_t)t * kBK;
-
-    // S^T = K Q^T, operands software-pipelined: the K chunks of step kk+1
-    // are read from LDS while the two (independent) products of step kk run
+  // S^T = K Q^T of the tile in Ks, operands software-pipelined: the K chunks
+  // of step kk+1 are read from LDS while the two (independent) products of
+  // step kk run; then the keys past a row's last visible key are masked
+  auto scores = [&](const char* Ks, int64_t k0, f32x16 (&s)[2]) {
     const int kr0 = perm_row(n);  // K row of this lane in block mb: 32*mb + kr0
     const int ksw = swz_k<D>(kr0);  // the same swizzle for both blocks (32 = 0 mod 16)
     const char* krow = Ks + kr0 * TL::ROWB;
     auto kread = [&](int kk, int mb) {
       return *(const lds_bf16x8*)(krow + mb * 32 * TL::ROWB + 16 * ((2 * kk + hh) ^ ksw));
     };
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    s[0] = f32x16{};
+    s[1] = f32x16{};
     bf16x8 kc0 = kread(0, 0), kc1 = kread(0, 1);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -266,6 +266,68 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(PrefillArgs a
         kc1 = kn1;
       }
     }
+  };
+  auto mask = [&](int64_t k0, f32x16 (&s)[2]) {
+    if (k0 + kBK > kfull) {  // tile reaches past the keys every row sees: mask per element
+      // last visible key in the tile, relative to this lane's first key (8*hh)
+      const int rel = (int)max(min(lim - k0, (int64_t)kBK), (int64_t)-1) - 8 * hh;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * mb + 16 * (i >> 3) + (i & 7) > rel) s[mb][i] = -INFINITY;
+    }
+  };
+  // moves the reference m to the tile's scaled max when that exceeds m + thr
+  // (log2 units) for some row of the wave, rescaling the accumulators
+  auto rebase = [&](const f32x16 (&s)[2], float thr) {
+    float tmax = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) tmax = fmaxf(fmaxf(tmax, s[0][i]), s[0][i + 1]);
+    tmax = fmaxf(fmaxf(tmax, s[0][15]), s[1][0]);
+#pragma unroll
+    for (int i = 1; i < 15; i += 2) tmax = fmaxf(fmaxf(tmax, s[1][i]), s[1][i + 1]);
+    tmax = fmaxf(tmax, s[1][15]);
+    tmax = half_swap_max(tmax);
+    const float tx = tmax * a.scale_log2;
+    if (__builtin_amdgcn_ballot_w64(tx > m + thr) != 0) {
+      const float m_new = fmaxf(m, tx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    }
+  };
+  // weights against the reference mu: bf16 copies and this lane's sum
+  auto weights = [&](const f32x16 (&s)[2], float mu, bf16x8 (&pf)[4]) {
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][i], a.scale_log2, -mu));
+        ps[i & 3] += p;
+        pf[2 * mb + (i >> 3)][i & 7] = (__bf16)p;
+      }
+    }
+    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+
+  // FIRST: the first tile sets the reference from its max.  Later tiles use
+  // the reference as it stands and only check that the weights stayed
+  // finite: m need not be the running max, only keep the weights in range,
+  // so it moves only when a lane's part of a tile sum leaves (0, 2^32] (or
+  // is not a number: also when m is still -inf).  Then the scores are
+  // computed again from the tile, still in LDS, and the reference moved to
+  // their max.  Any reference gives the exact result; the final lse uses the
+  // one actually applied.
+  auto tile_step = [&](auto first, int t, const char* Ks, char* next) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t have landed
+    __syncthreads();                     // ... everyone's; and tile t-1 is fully consumed
+    const int64_t k0 = (int64_t)t * kBK;
+    f32x16 s[2];
+    scores(Ks, k0, s);
 
     // V^T operand (key chunk c of 16, output rows 32*db ..) by two transposing reads
     auto vread = [&](int c, int db) {
@@ -285,50 +347,29 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(PrefillArgs a
     __builtin_amdgcn_sched_barrier(0);
     if (t + 1 < ntiles) issue_tile(t + 1, next);
 
-    if (k0 + kBK > kfull) {  // tile reaches past the keys every row sees: mask per element
-      // last visible key in the tile, relative to this lane's first key (8*hh)
-      const int rel = (int)max(min(lim - k0, (int64_t)kBK), (int64_t)-1) - 8 * hh;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * mb + 16 * (i >> 3) + (i & 7) > rel) s[mb][i] = -INFINITY;
-    }
-    float tmax = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-#pragma unroll
-    for (int i = 3; i < 15; i += 2) tmax = fmaxf(fmaxf(tmax, s[0][i]), s[0][i + 1]);
-    tmax = fmaxf(fmaxf(tmax, s[0][15]), s[1][0]);
-#pragma unroll
-    for (int i = 1; i < 15; i += 2) tmax = fmaxf(fmaxf(tmax, s[1][i]), s[1][i + 1]);
-    tmax = fmaxf(tmax, s[1][15]);
-    tmax = half_swap_max(tmax);
-    // scale > 0, so the max of the raw scores times scale*log2(e) is the scaled max.
-    // The reference max m only moves when a tile exceeds it by more than 8
-    // (log2 units): p then stays <= 256 and the rescale of the accumulators is
-    // skipped for the whole wave on most tiles.  Any reference gives the
-    // exact result; the final lse uses the one actually applied.
-    const float tx = tmax * a.scale_log2;
-    if (__builtin_amdgcn_ballot_w64(tx > m + 8.f) != 0) {
-      const float m_new = fmaxf(m, tx);
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
-      m = m_new;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-    }
-    const float m_use = m == -INFINITY ? 0.f : m;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    mask(k0, s);
     bf16x8 pf[4];
+    float lt;
+    if constexpr (decltype(first)::value) {
+      rebase(s, 0.f);
+      lt = weights(s, m == -INFINITY ? 0.f : m, pf);
+    } else {
+      lt = weights(s, m, pf);
+      if (__builtin_amdgcn_ballot_w64(!(lt <= 0x1p32f)) != 0) {
+        // (the V operands are read again afterwards, so they need no
+        // registers while the scores are recomputed)
+        f32x16 s2[2];
+        scores(Ks, k0, s2);
+        mask(k0, s2);
+        rebase(s2, 0.f);
+        lt = weights(s2, m == -INFINITY ? 0.f : m, pf);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][i], a.scale_log2, -m_use));
-        ps[i & 3] += p;
-        pf[2 * mb + (i >> 3)][i & 7] = (__bf16)p;
+          for (int db = 0; db < NDB; ++db) vt[c][db] = vread(c, db);
       }
     }
-    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    l += lt;
     // O^T += V^T P^T
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -336,10 +377,13 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_bf16_kernel(PrefillArgs a
       for (int db = 0; db < NDB; ++db) acc[db] = mfma32(vt[c][db], pf[c], acc[db]);
   };
 
-  if (ntiles > 0) issue_tile(0, stage0);
-  for (int t = 0; t < ntiles; t += 2) {
-    tile_step(t, stage0, stage1);
-    if (t + 1 < ntiles) tile_step(t + 1, stage1, stage0);
+  if (ntiles > 0) {
+    issue_tile(0, stage0);
+    tile_step(std::true_type{}, 0, stage0, stage1);
+  }
+  for (int t = 1; t < ntiles; t += 2) {
+    tile_step(std::false_type{}, t, stage1, stage0);
+    if (t + 1 < ntiles) tile_step(std::false_type{}, t + 1, stage0, stage1);
   }
 
   const float lt = half_swap_sum(l);

@@ -189,6 +189,23 @@ def test_prefill_peaked_and_needle_variants():
     check_lp(o, lse, ro, rl, "needles")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_rising_scores(causal):
+    """Scores that rise by ~37 log2 units from one 64-key tile to the next
+    (every query row all ones, key j = 0.05 j in every dim): each tile's weights
+    against the reference set by the tile before would pass 2^32, so every
+    tile takes the kernel's recompute-and-rebase path."""
+    import oracle
+    case = gen.prefill_inputs(1, 2, 1, 300, 300, 64, kind="bf16", seed=9)
+    q = np.full_like(case["q"], 0x3F80)  # bf16 1.0
+    kf = (0.05 * np.arange(300, dtype=np.float32))[None, :, None, None] * np.ones((1, 300, 1, 64), np.float32)
+    k = (kf.view(np.uint32) >> 16).astype(np.uint16)  # truncation to bf16 (the oracle sees the same bits)
+    c = dict(case, q=q, k=k)
+    o, lse = gpu_prefill(c, causal)
+    ro, rl = oracle.prefill(c, causal=causal)
+    check_lp(o, lse, ro, rl, f"rising scores causal={causal}")
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_prefill_llama13b_full_size_every_row():

@@ -25,6 +25,8 @@
 // of 8 consecutive keys, the B operand of the P.V product.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace attn {
@@ -216,13 +218,9 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fp8_kernel(PrefillArgs a,
   const int v_chunk = g16 & 1;  // + 2*db
   const int v_half = 8 * (i16 & 1);
 
-  auto tile_step = [&](int t, const char* Ks, char* next) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t have landed
-    __syncthreads();
-    const char* Vs = Ks + TL::BYTES;
-    const int64_t k0 = (int64_t)t * kBK;
-
-    // S^T = K Q^T
+  // S^T = K Q^T of the tile in Ks, then the keys past a row's last visible
+  // key masked
+  auto scores = [&](const char* Ks, int64_t k0, f32x16 (&s)[2]) {
     const int kr0 = perm_row(n);
     const int ksw = swz_k<D>(kr0);  // the same swizzle for both blocks (rows 32 apart)
     const char* krow = Ks + kr0 * TL::ROWB;
@@ -233,13 +231,73 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fp8_kernel(PrefillArgs a,
       const i32x4 hi = *(const lds_i32x4*)(base + 16 * ((c0 + 1) ^ ksw));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const i32x8 k0v = kread(kk, 0), k1v = kread(kk, 1);
       s[0] = mfma_fp8(k0v, qf[kk], s[0]);
       s[1] = mfma_fp8(k1v, qf[kk], s[1]);
     }
+  };
+  auto mask = [&](int64_t k0, f32x16 (&s)[2]) {
+    if (k0 + kBK > kfull) {  // mask per element past the keys every row sees
+      const int rel = (int)max(min(lim - k0, (int64_t)kBK), (int64_t)-1) - 8 * hh;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * mb + 16 * (i >> 3) + (i & 7) > rel) s[mb][i] = -INFINITY;
+    }
+  };
+  // moves the reference m to the tile's scaled max (qk_mul > 0: the max of
+  // the raw scores times qk_mul) where that exceeds m for some row of the
+  // wave, rescaling the accumulators
+  auto rebase = [&](const f32x16 (&s)[2]) {
+    float tmax = s[0][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s[0][i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[1][i]);
+    tmax = half_swap_max(tmax);
+    const float tx = tmax * qk_mul;
+    if (__builtin_amdgcn_ballot_w64(tx > m) != 0) {
+      const float m_new = fmaxf(m, tx);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+    }
+  };
+  auto weights = [&](const f32x16 (&s)[2], float mu, bf16x8 (&pf)[4]) {
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][i], qk_mul, -mu));
+        ps[i & 3] += p;
+        pf[2 * mb + (i >> 3)][i & 7] = (__bf16)p;
+      }
+    }
+    return (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+
+  // The first tile sets the reference m from its max.  Later tiles use the
+  // reference as it stands and only check that the weights stayed finite (m
+  // need not be the running max, only keep the weights in range): when a
+  // lane's part of a tile sum leaves (0, 2^32] (or is not a number, as while
+  // m is still -inf), the scores are computed again from the tile, still in
+  // LDS, and m moves to their max.  Any reference gives the exact result;
+  // the final lse uses the one actually applied.
+  auto tile_step = [&](auto first, int t, const char* Ks, char* next) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile t have landed
+    __syncthreads();
+    const char* Vs = Ks + TL::BYTES;
+    const int64_t k0 = (int64_t)t * kBK;
+    f32x16 s[2];
+    scores(Ks, k0, s);
 
     // raw V^T operands of the tile (key chunk c of 16, output rows 32*db ..),
     // read before the next tile's copies are issued
@@ -255,44 +313,23 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fp8_kernel(PrefillArgs a,
     __builtin_amdgcn_sched_barrier(0);
     if (t + 1 < ntiles) issue_tile(t + 1, next);
 
-    if (k0 + kBK > kfull) {  // mask per element past the keys every row sees
-      const int rel = (int)max(min(lim - k0, (int64_t)kBK), (int64_t)-1) - 8 * hh;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * mb + 16 * (i >> 3) + (i & 7) > rel) s[mb][i] = -INFINITY;
-    }
-    float tmax = s[0][0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s[0][i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[1][i]);
-    tmax = half_swap_max(tmax);
-    // qk_mul > 0: the scaled max is the max of the raw scores times qk_mul; the
-    // reference max moves only when a tile exceeds it by more than 8 (log2 units)
-    const float tx = tmax * qk_mul;
-    if (__builtin_amdgcn_ballot_w64(tx > m + 8.f) != 0) {
-      const float m_new = fmaxf(m, tx);
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
-      m = m_new;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
-    }
-    const float m_use = m == -INFINITY ? 0.f : m;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    mask(k0, s);
     bf16x8 pf[4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][i], qk_mul, -m_use));
-        ps[i & 3] += p;
-        pf[2 * mb + (i >> 3)][i & 7] = (__bf16)p;
+    float lt;
+    if constexpr (decltype(first)::value) {
+      rebase(s);
+      lt = weights(s, m == -INFINITY ? 0.f : m, pf);
+    } else {
+      lt = weights(s, m, pf);
+      if (__builtin_amdgcn_ballot_w64(!(lt <= 0x1p32f)) != 0) {
+        f32x16 s2[2];
+        scores(Ks, k0, s2);
+        mask(k0, s2);
+        rebase(s2);
+        lt = weights(s2, m == -INFINITY ? 0.f : m, pf);
       }
     }
-    l += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    l += lt;
     // O^T += V^T P^T
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -300,10 +337,13 @@ __global__ void __launch_bounds__(kThreads, 2) prefill_fp8_kernel(PrefillArgs a,
       for (int db = 0; db < NDB; ++db) acc[db] = mfma_bf16(fp8x8_to_bf16(vraw[c][db]), pf[c], acc[db]);
   };
 
-  if (ntiles > 0) issue_tile(0, stage0);
-  for (int t = 0; t < ntiles; t += 2) {
-    tile_step(t, stage0, stage1);
-    if (t + 1 < ntiles) tile_step(t + 1, stage1, stage0);
+  if (ntiles > 0) {
+    issue_tile(0, stage0);
+    tile_step(std::true_type{}, 0, stage0, stage1);
+  }
+  for (int t = 1; t < ntiles; t += 2) {
+    tile_step(std::false_type{}, t, stage1, stage0);
+    if (t + 1 < ntiles) tile_step(std::false_type{}, t + 1, stage0, stage1);
   }
 
   const float lt = half_swap_sum(l);

@@ -120,6 +120,22 @@ def test_prefill_fp8_shapes(B, Hq, Hkv, S, T, D, causal):
     check_lp(o, lse, ro, rl, f"fp8 {B,Hq,Hkv,S,T,D,causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_fp8_rising_scores(causal):
+    """e4m3 scores rising by ~37 log2 units from one 64-key tile to the next
+    (query rows all ones, key j = e4m3(0.05 j) in every dim, unit scales): every
+    tile takes the fp8 kernel's recompute-and-rebase path."""
+    import oracle
+    case = gen.prefill_inputs(1, 2, 1, 300, 300, 64, kind="fp8", seed=9)
+    q = np.full_like(case["q"], gen.encode_e4m3fn(np.array([1.0]))[0])
+    kf = (0.05 * np.arange(300))[None, :, None, None] * np.ones((1, 300, 1, 64))
+    c = dict(case, q=q, k=gen.encode_e4m3fn(kf), q_scale=np.ones_like(case["q_scale"]),
+             k_scale=np.ones_like(case["k_scale"]))
+    o, lse = gpu_prefill_fp8(c, causal)
+    ro, rl = oracle.prefill(c, causal=causal)
+    check_lp(o, lse, ro, rl, f"fp8 rising scores causal={causal}")
+
+
 def rows_in_every_tile(S, G, seed, tile_rows=128):
     """Query positions hitting every tile of `tile_rows` packed rows r = pos * G + g
     (one random packed row per tile, mapped to its position), plus 0 and S - 1."""

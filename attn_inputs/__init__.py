@@ -294,7 +294,7 @@ def sample_rows(S, n, seed):
     return np.sort(np.concatenate([[0, S - 1], inner]).astype(np.int64))
 
 
-# BASELINE workloads by name (shapes from the pages' LLaMa-13B / 512-token-page settings)
+# The benchmark and parity workloads by name (shapes from the pages' LLaMa-13B / 512-token-page settings)
 WORKLOADS = {
     "tiny_gqa_causal_f32": dict(B=1, Hq=4, Hkv=2, S=256, T=256, D=64, kind="f32", causal=True),
     "llama13b_gqa_causal_bf16": dict(B=4, Hq=40, Hkv=8, S=4096, T=4096, D=128, kind="bf16", causal=True),

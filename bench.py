@@ -700,7 +700,7 @@ def main():
                     help="also run a plain 1 GiB device-to-device copy three times (PMC byte-counter reference)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (sharding is a design note only); "
+        print("bench.py measures one GPU: the library has no multi-GPU path (sharding is a design note only); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

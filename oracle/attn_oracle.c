@@ -27,7 +27,8 @@
  *    (FP8 KV).  int8: value = code * per-(token, KV head) scale.  fp8: OCP
  *    e4m3fn (bias 7, no infinities, S.1111.111 = NaN) times a per-KV-head
  *    scale.  int4 (named beside int8 in the ONNX Runtime PR #28695
- *    analysis, introduction; the layout is this build's reading): signed
+ *    analysis, introduction; the page fixes no layout, so this one is a
+ *    plain reading of it): signed
  *    two's-complement 4-bit codes, element 2i in the low nibble of byte i and
  *    element 2i+1 in its high nibble, value = code * the scale of the
  *    element's 32-element group of its (token, KV head) row;

@@ -240,7 +240,8 @@ def bench_prefill_f32(args):
             "us_per_launch": round(ms * 1e3, 3), "flop_per_launch": flops,
             "roofline": {"bound": "alu", "achieved": round(tflops, 4), "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / PEAK_FP32_TFLOPS, 5), "traffic": None,
-                         "note": "a 128-work-group launch: information only, bound by launch and latency"}}
+                         "note": "128 work-groups of 8 packed rows, keys split over each one's 4 waves: "
+                                 "information only, bound by launch and latency"}}
 
 
 def bench_prefill_fp8(args):

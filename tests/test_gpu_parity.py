@@ -74,6 +74,26 @@ def test_prefill_f32_shapes(B, Hq, Hkv, S, T, D, causal):
     check_f32(o, lse, ro, rl, f"f32 {B,Hq,Hkv,S,T,D,causal}")
 
 
+# The fp32 launches above are small: their row tiles would leave compute units
+# idle, so they run on the key-split kernel.  These shapes make at least 512
+# row tiles (two per compute unit of a 256-CU device) and run the row-tile
+# kernel; every 8th query row is compared with the oracle.
+@pytest.mark.parametrize("B,Hq,Hkv,S,T,D,causal", [
+    (2, 16, 8, 4096, 256, 64, False),   # 8192 packed rows per KV head / 256 = 32 tiles x 16
+    (2, 32, 8, 1024, 1024, 128, True),  # 4096 packed rows per KV head / 128 = 32 tiles x 16
+    (2, 32, 8, 1031, 700, 128, True)])  # dead leading rows, ragged tiles
+def test_prefill_f32_row_tiles(B, Hq, Hkv, S, T, D, causal):
+    case = gen.prefill_inputs(B, Hq, Hkv, S, T, D, kind="f32", seed=11 + S + T)
+    o, lse = gpu_prefill(case, causal)
+    import oracle
+    rows = np.arange(0, S, 8)
+    if rows[-1] != S - 1:
+        rows = np.append(rows, S - 1)
+    ro, rl = oracle.prefill(case, causal=causal, rows=rows)
+    check_f32(o[:, rows], lse[:, :, rows], ro, rl, f"f32 row tiles {B,Hq,Hkv,S,T,D,causal}")
+    assert np.all(np.isfinite(o))
+
+
 BF16_SHAPES = [
     (1, 4, 2, 256, 256, 64, True),     # several tiles, D=64
     (2, 10, 2, 300, 300, 128, True),   # G = 5, ragged tails
@@ -580,6 +600,26 @@ def test_stream_budgeted_small(kind):
     o_again, _, _ = attn.stream_budgeted(qh, kh, vh, causal=True, scale=case["scale"], budget=64 << 20,
                                          block_q=256, block_k=128)
     assert np.array_equal(o_again.numpy(), outs[0])
+
+
+def test_stream_f32_large_blocks():
+    """fp32 streaming whose sub-tasks are large enough for the row-tile kernel
+    (2048 x 4 packed rows per KV head: 64 tiles x 8 heads), so the accumulate
+    mode of that kernel is checked: == the unbudgeted device run, == the oracle
+    on sampled rows."""
+    import oracle
+    B, Hq, Hkv, S, T, D = 1, 32, 8, 4096, 4096, 128
+    case = gen.prefill_inputs(B, Hq, Hkv, S, T, D, kind="f32", seed=47)
+    qh, kh, vh = (_pinned(case[n]) for n in "qkv")
+    o_dev, l_dev = gpu_prefill(case)
+    o, lse, rep = attn.stream_budgeted(qh, kh, vh, causal=True, scale=case["scale"], budget=1 << 30,
+                                       block_q=2048, block_k=1024)
+    o, lse = o.numpy(), lse.numpy()
+    say(f"stream f32 2048x1024: {rep}")
+    assert max_abs_err(o, o_dev) <= 1e-5 and lse_err(lse, l_dev) <= 1e-4
+    rows = np.concatenate([np.arange(0, S, 64), [1023, 1024, 2047, 2048, S - 1]])
+    ro, rl = oracle.prefill(case, rows=rows)
+    check_f32(o[:, rows], lse[:, :, rows], ro, rl, "stream f32 large blocks")
 
 
 def test_stream_rejects_pageable_host_memory():

@@ -42,9 +42,11 @@
 // every pipeline stage.
 //
 // Each of the 4 waves of a work-group scans every 4th 32-token block of a
-// piece with its own online softmax; blocks load one (bf16) or two (smaller
-// tiles) ahead of the one consumed.  The waves are then combined through
-// LDS and the piece's record (or the final output) written.
+// piece with its own online softmax (a per-row reference m that moves only
+// when a block's weights would leave a safe range, as in the prefill
+// kernels); blocks load one (bf16) or two (smaller tiles) ahead of the one
+// consumed.  The waves are then combined through LDS and the piece's record
+// (or the final output) written.
 #include <math.h>
 #include <stdlib.h>
 
@@ -556,19 +558,30 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) sc[e] = g0 + 8 * j + e < lim ? sc[e] : -INFINITY;
         }
-        float mx = sc[0];
+        // The weights against the reference m as it stands.  Any m gives the
+        // exact result while the weights stay finite (the lse uses the m
+        // applied), so m moves only when a lane's weights would pass 2^32,
+        // or while it is still -inf (the weights are then inf or NaN): then
+        // it becomes the block's row max and the weights are taken again.
+        float pv[8];
+        float ls = 0.f;
 #pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
-        {
-          float u0, u1;
-          lane_pair<16>(mx, u0, u1);
-          mx = fmaxf(u0, u1);
-          lane_pair<32>(mx, u0, u1);
-          mx = fmaxf(u0, u1);
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], smul, -m));
+          ls += pv[e];
         }
-        const float tx = mx * smul;
-        if (__builtin_amdgcn_ballot_w64(tx > m + 8.f) != 0) {
-          const float m_new = fmaxf(m, tx);
+        if (__builtin_amdgcn_ballot_w64(!(ls <= 0x1p32f)) != 0) {
+          float mx = sc[0];
+#pragma unroll
+          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[e]);
+          {
+            float u0, u1;
+            lane_pair<16>(mx, u0, u1);
+            mx = fmaxf(u0, u1);
+            lane_pair<32>(mx, u0, u1);
+            mx = fmaxf(u0, u1);
+          }
+          const float m_new = fmaxf(m, mx * smul);
           const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
           m = m_new;
           l *= alpha;
@@ -578,20 +591,22 @@ __global__ void __launch_bounds__(kThreads) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int c = 0; c < TL::CPR; ++c) corr[c] *= alpha;
           }
+          const float m_use = m == -INFINITY ? 0.f : m;
+          ls = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[e], smul, -m_use));
+            ls += pv[e];
+          }
         }
-        const float m_use = m == -INFINITY ? 0.f : m;
         // the weights as a bf16 pair hi + lo (lo = the rounding residue of
         // hi): two P.V products carry them to ~2^-17 relative, where bf16
         // alone would err by 2^-9 of each weight times |v|.  The scan is
         // bound by HBM, so the second product is free.
         bf16x8 pf, plo;
-        float pv[8];
-        float ls = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          float p = __builtin_amdgcn_exp2f(fmaf(sc[e], smul, -m_use));
-          ls += p;
-          pv[e] = p;
+          float p = pv[e];
           if constexpr (KV == ATTN_INT8) p = sc[e] == -INFINITY ? 0.f : p * vsc[e];
           pf[e] = (__bf16)p;
           plo[e] = (__bf16)(p - (float)pf[e]);

@@ -1,9 +1,11 @@
 // Tiled exact attention prefill, bf16 operands on gfx950 matrix cores.
 //
-// One pass over key tiles with an online softmax (running row max m and row
-// sum l, rescaling the fp32 output accumulator by exp(m_old - m_new)), the
-// P.V product accumulated in fp32: the tiled flash-attention scheme of the
-// ONNX Runtime PR #28695 analysis (section 1), laid out for CDNA4 waves.
+// One pass over key tiles with an online softmax (a per-row reference m and
+// row sum l, rescaling the fp32 output accumulator by exp(m_old - m_new) when
+// m moves), the P.V product accumulated in fp32: the tiled flash-attention
+// scheme of the ONNX Runtime PR #28695 analysis (section 1), laid out for
+// CDNA4 waves.  m is the first tile's row max and moves only when a tile's
+// weights would leave a safe range (below), not on every new maximum.
 //
 // Work decomposition
 //   grid = (row tiles, Hkv, B).  A work-group serves ONE KV head and a tile of

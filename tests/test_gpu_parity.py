@@ -242,6 +242,31 @@ def test_prefill_rising_scores(causal):
     check_lp(o, lse, ro, rl, f"rising scores causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_f32_rising_and_falling_scores(causal):
+    """fp32 key-split kernel: scores that rise along the keys by 1.28 per
+    64-key tile (each wave's running max moves on every tile) to 4, then fall
+    to -4, so the waves' maxima differ and causal rows leave some waves with
+    no key.  (Scores stay small: an fp32 score of size s carries a rounding
+    error of ~s * 2^-24, which moves the output by about as much, and the
+    fp32 bar is 1e-4 of max(|O|, 0.01).)"""
+    import oracle
+    case = gen.prefill_inputs(1, 4, 2, 300, 300, 64, kind="f32", seed=13)
+    q = np.ones_like(case["q"])
+    ramp = np.concatenate([0.0025 * np.arange(200), 0.5 - 0.01 * np.arange(100)]).astype(np.float32)
+    k = ramp[None, :, None, None] * np.ones((1, 300, 2, 64), np.float32)
+    c = dict(case, q=q, k=k)
+    o, lse = gpu_prefill(c, causal)
+    ro, rl = oracle.prefill(c, causal=causal)
+    check_f32(o, lse, ro, rl, f"f32 rising/falling scores causal={causal}")
+
+
+def test_prefill_f32_empty_keys():
+    case = gen.prefill_inputs(1, 4, 2, 10, 0, 64, kind="f32", seed=5)
+    o, lse = gpu_prefill(case, True)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_prefill_llama13b_full_size_every_row():

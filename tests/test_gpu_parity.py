@@ -65,7 +65,7 @@ def test_prefill_tiny_gqa_causal_f32():
 
 @pytest.mark.parametrize("B,Hq,Hkv,S,T,D,causal", [
     (2, 6, 3, 77, 133, 128, True), (1, 4, 4, 200, 200, 64, False), (1, 2, 1, 300, 40, 64, True),
-    (1, 5, 5, 1, 97, 128, True)])
+    (1, 5, 5, 1, 97, 128, True), (2, 10, 2, 77, 133, 64, True)])
 def test_prefill_f32_shapes(B, Hq, Hkv, S, T, D, causal):
     case = gen.prefill_inputs(B, Hq, Hkv, S, T, D, kind="f32", seed=3 + S + T)
     o, lse = gpu_prefill(case, causal)
@@ -625,6 +625,28 @@ def test_stream_budgeted_small(kind):
     o_again, _, _ = attn.stream_budgeted(qh, kh, vh, causal=True, scale=case["scale"], budget=64 << 20,
                                          block_q=256, block_k=128)
     assert np.array_equal(o_again.numpy(), outs[0])
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f32"])
+def test_stream_budgeted_d64(kind):
+    """D = 64 streaming (G = 4, S != T, blocks that do not divide the sequence)
+    == the unbudgeted device run and the oracle."""
+    import oracle
+    B, Hq, Hkv, S, T, D = 2, 8, 2, 500, 700, 64
+    case = gen.prefill_inputs(B, Hq, Hkv, S, T, D, kind=kind, seed=53)
+    qh, kh, vh = (_pinned(case[n]) for n in "qkv")
+    o_dev, l_dev = gpu_prefill(case)
+    ro, rl = oracle.prefill(case)
+    o, lse, rep = attn.stream_budgeted(qh, kh, vh, causal=True, scale=case["scale"], budget=64 << 20,
+                                       block_q=192, block_k=160)
+    o, lse = o.numpy(), lse.numpy()
+    say(f"stream {kind} D=64: {rep}")
+    if kind == "f32":
+        check_f32(o, lse, ro, rl, "stream f32 D=64")
+    else:
+        check_lp(o, lse, ro, rl, "stream bf16 D=64")
+    tol = 1e-5 if kind == "f32" else 5e-3
+    assert max_abs_err(o, o_dev) <= tol and lse_err(lse, l_dev) <= (1e-4 if kind == "f32" else 1e-3)
 
 
 def test_stream_f32_large_blocks():

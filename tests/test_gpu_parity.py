@@ -627,12 +627,13 @@ def test_stream_budgeted_small(kind):
     assert np.array_equal(o_again.numpy(), outs[0])
 
 
-@pytest.mark.parametrize("kind", ["bf16", "f32"])
-def test_stream_budgeted_d64(kind):
-    """D = 64 streaming (G = 4, S != T, blocks that do not divide the sequence)
-    == the unbudgeted device run and the oracle."""
+@pytest.mark.parametrize("kind,S,T", [("bf16", 500, 700), ("f32", 500, 700), ("bf16", 700, 500)])
+def test_stream_budgeted_d64(kind, S, T):
+    """D = 64 streaming (G = 4, S != T, blocks that do not divide the sequence;
+    S > T leaves the first S - T query rows with no key) == the unbudgeted
+    device run and the oracle."""
     import oracle
-    B, Hq, Hkv, S, T, D = 2, 8, 2, 500, 700, 64
+    B, Hq, Hkv, D = 2, 8, 2, 64
     case = gen.prefill_inputs(B, Hq, Hkv, S, T, D, kind=kind, seed=53)
     qh, kh, vh = (_pinned(case[n]) for n in "qkv")
     o_dev, l_dev = gpu_prefill(case)
@@ -640,7 +641,9 @@ def test_stream_budgeted_d64(kind):
     o, lse, rep = attn.stream_budgeted(qh, kh, vh, causal=True, scale=case["scale"], budget=64 << 20,
                                        block_q=192, block_k=160)
     o, lse = o.numpy(), lse.numpy()
-    say(f"stream {kind} D=64: {rep}")
+    say(f"stream {kind} D=64 S={S} T={T}: {rep}")
+    if S > T:
+        assert np.all(o[:, :S - T] == 0) and np.all(np.isneginf(lse[:, :, :S - T]))
     if kind == "f32":
         check_f32(o, lse, ro, rl, "stream f32 D=64")
     else:
